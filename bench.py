@@ -1,0 +1,182 @@
+"""Batch-1 decode benchmark on one MI355X.
+
+A step is one decoded token: one pass of the whole hot path (embedding,
+every layer's RMSNorm/QKV/RoPE+KV append/split-K attention/O/SwiGLU FFN,
+final norm, lm_head, argmax and on-device feedback).  All K timed steps run
+inside ONE kie_decode call, i.e. one persistent kernel launch.
+
+Prints one JSON line: tokens/s, ms per token, the HBM roofline of the
+decode kernel (algorithmic bytes per launch / launch time vs 8 TB/s), and
+the CPU oracle timed on the host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs ~8 TB/s peak, ~2.2B fp16"
+
+
+def weight_bytes_per_token(c) -> int:
+    """fp16 bytes of every weight one decode step reads (active experts only)."""
+    d, qd, kd = c.d_model, c.n_heads * c.head_dim, c.n_kv_heads * c.head_dim
+    per_layer = (qd * d + 2 * kd * d + d * qd) + 2 * d            # attention + 2 norm gains
+    if c.n_experts:
+        per_layer += c.n_experts * d + (c.top_k + c.n_shared_experts) * 3 * c.expert_hidden * d
+    else:
+        per_layer += 3 * c.ffn_hidden * d
+    total = c.n_layers * per_layer + d + c.vocab_out * d + d         # final norm, lm_head, emb row
+    return 2 * total
+
+
+def kv_bytes_per_position(c) -> int:
+    return 2 * c.n_layers * c.n_kv_heads * c.head_dim * 2            # K and V, fp16
+
+
+def decode_bytes(c, pos0: int, n: int) -> int:
+    """Algorithmic HBM bytes of n decode steps starting at position pos0: all
+    weights, plus at position p the p cached K/V rows read and 1 row written."""
+    W = weight_bytes_per_token(c)
+    kv = kv_bytes_per_position(c)
+    rows = sum(p + 1 for p in range(pos0, pos0 + n))
+    return n * W + kv * rows
+
+
+def cpu_baseline(cfg, W, prompt, budget_s: float):
+    """The oracle as it stands, timed on this host: decode steps after a short
+    batched prefill, until about budget_s seconds of decode have run."""
+    import numpy as np
+    from oracle import Oracle
+    from kie_synth import weights_to_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    Wn = weights_to_numpy(W)
+    o = Oracle(cfg, Wn)
+    p_len = min(64, len(prompt))
+    o.prefill(prompt[:p_len])
+    o.decode(1)                                 # widens the remaining weights once
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        o.decode(1)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or o.pos >= cfg.kv_capacity - 1:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": (f"{cfg.name}: numpy fp32 oracle, {n} greedy decode steps after a "
+                       f"{p_len}-token batched prefill ({el:.1f} s on {cores} host cores, "
+                       f"BLAS threads {threads})"),
+            "ms_per_token": 1e3 * el / n}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default: the config's)")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="2b")
+    ap.add_argument("--graph", action="store_true", help="staged per-kernel hipGraph mode")
+    ap.add_argument("--reps", type=int, default=3, help="timed repetitions (median reported)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (batch-1 decode on a single "
+              "MI355X); multi-GPU tensor parallelism is not built. Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import persistent_decode_monokernel_amd as kie
+    from kie_synth import get_config, make_prompt, make_weights
+
+    cfg = get_config(args.config)
+    K = args.steps if args.steps is not None else cfg.n_decode
+    P = cfg.prompt_len
+    max_seq = max(cfg.kv_capacity, P + max(K, args.warmup))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = make_weights(cfg, seed=0, device=dev)
+    prompt = make_prompt(cfg, seed=0)
+    stream = torch.cuda.current_stream()
+
+    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph)
+    eng.prefill(prompt)
+    if args.warmup:
+        eng.decode(args.warmup, logits=False)
+    toks = torch.empty(K, dtype=torch.int32, device=dev)
+    times, kernel_ms = [], []
+    for _ in range(max(1, args.reps)):
+        eng.reset()
+        eng.prefill(prompt)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        eng.decode_into(K, toks, None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        kernel_ms.append(eng.last_elapsed_ms())
+    med = sorted(range(len(times)), key=lambda i: times[i])[len(times) // 2]
+    ms = times[med]
+    kms = kernel_ms[med]
+    tok_s = K / (ms / 1e3)
+    nbytes = decode_bytes(cfg, P - 1, K)
+    achieved = nbytes / (kms / 1e3) / 1e9
+    eng.close()
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: {cfg.n_layers} layers, d_model {cfg.d_model}, "
+                                f"{cfg.n_heads}x{cfg.head_dim} heads ({cfg.n_kv_heads} KV), "
+                                + (f"MoE {cfg.n_experts}e top{cfg.top_k}+{cfg.n_shared_experts} "
+                                   f"hidden {cfg.expert_hidden}" if cfg.n_experts else
+                                   f"SwiGLU {cfg.ffn_hidden}")
+                                + f", vocab {cfg.vocab_out}; batch 1, prompt {P}, greedy decode "
+                                  f"{K}; fp16 weights N(0,0.02) seed 0, fp16 KV"),
+                   "global_batch": 1, "seq_len": P + K,
+                   "mode": "staged-hipgraph" if args.graph else "persistent"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "detail": {"kernel": "kie::mono_kernel" if not args.graph else "kie::stage_kernel",
+                   "bytes_per_launch": nbytes, "bytes_per_token": nbytes / K,
+                   "kernel_ms": kms, "call_ms": ms, "reps_call_ms": times,
+                   "roofline_tok_s": HBM_PEAK_GBS * 1e9 / (nbytes / K)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, W, prompt, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,185 @@
+/*
+ * kie.h — C ABI of libkie.so: batch-1 decode of an fp16 decoder-only
+ * transformer as one GPU-resident persistent kernel on MI355X (gfx950).
+ *
+ * What the library does
+ *   The pages describe a "persistent monokernel": one GPU-resident program
+ *   that runs the whole decode path (matrix multiplies, attention,
+ *   normalisation and sampling) and never hands control back to the CPU
+ *   between tokens (page "Breaking the memory wall: 3,000 tokens/s on
+ *   standard GPUs", agentlenshq.com, section "1. The Monokernel Runtime").
+ *   They name the overheads it removes: ~4.5 us per kernel launch,
+ *   host-side scheduling and CPU sampling, and grid-wide synchronisation
+ *   (same page, section "Where the microseconds are lost").  kie_decode()
+ *   runs n_steps tokens in ONE kernel launch; token feedback (greedy argmax)
+ *   stays on the device.
+ *
+ * Model (the pages give no layer equations; the plain pre-norm reading):
+ *   x = E[tok];  per layer:  x += Wo·Attn(RoPE(Wq·rms(x)), RoPE(Wk·rms(x)), Wv·rms(x))
+ *                            x += FFN(rms(x))        (SwiGLU, or MoE below)
+ *   logits = Wlm·rms(x);  next token = argmax (lowest index on ties).
+ *   RMSNorm: x / sqrt(mean(x^2) + eps) * gain.  RoPE: rotate-half pairs
+ *   (j, j + head_dim/2), theta_j = base^(-2j/head_dim).  Attention scale
+ *   1/sqrt(head_dim), causal, query head i reads KV head i / (H / n_kv).
+ *   MoE FFN: p = softmax(Wr·h); the top_k largest p (lower id on ties) mix
+ *   with weights p (not renormalised), plus n_shared_experts always-on
+ *   experts with weight 1.  Only active experts are read, as the pages
+ *   stress that bandwidth follows active parameters (same page, section
+ *   "Scaling to frontier MoE models").
+ *
+ * Conventions
+ *   - All weights are fp16, row-major [out][in], in device memory owned by
+ *     the caller; they must outlive the handle.  The library never writes
+ *     or frees them.  Every GEMV input length (d_model, n_heads*head_dim,
+ *     ffn_hidden, expert_hidden) must be a multiple of 8 (16-byte rows).
+ *   - Activations are fp32; the KV cache is fp16 (round to nearest even).
+ *   - Prefill/decode split: after kie_prefill(t, P) the cache holds
+ *     positions 0..P-2 and t[P-1] is pending at position P-1.  Decode step
+ *     i runs the model on the pending token at position P-1+i, writes
+ *     out_tokens[i] = its greedy token g_i (and its logits) and makes g_i
+ *     pending.  decode(a) followed by decode(b) equals decode(a+b).
+ *   - Every call is synchronous: it returns after the device work is done,
+ *     so device-side errors (barrier watchdog) are reported by that call.
+ *     A handle is not thread-safe.
+ *   - Return value: KIE_OK (0) or a negative kie_status.  All argument
+ *     checks run before any launch, so a rejected call changes nothing.
+ *     kie_last_error() gives a message for the calling thread.
+ */
+#ifndef KIE_H
+#define KIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kie_status {
+  KIE_OK = 0,
+  KIE_ERR_INVALID_ARG = -1,      /* NULL pointer, bad shape, bad size          */
+  KIE_ERR_BAD_STATE = -2,        /* prefill on a used handle, decode w/o prompt,
+                                    or a handle broken by an earlier device error */
+  KIE_ERR_CONTEXT_OVERFLOW = -3, /* position would pass max_seq                */
+  KIE_ERR_TOKEN_RANGE = -4,      /* prompt token id outside [0, vocab_in)      */
+  KIE_ERR_OCCUPANCY = -5,        /* the grid cannot be co-resident             */
+  KIE_ERR_HIP = -6,              /* a HIP runtime call failed                  */
+  KIE_ERR_TIMEOUT = -7,          /* a device barrier wait passed timeout_ms    */
+  KIE_ERR_UNSUPPORTED = -8       /* shape outside what the kernels implement   */
+} kie_status;
+
+/* flags */
+#define KIE_MODE_GRAPH 0x1u   /* decode by replaying a hipGraph of per-stage
+                                 kernels (one kernel per stage) instead of one
+                                 persistent launch; same stage code, same
+                                 results bit for bit */
+
+typedef struct kie_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden;
+  int32_t vocab_in;          /* embedding rows                                 */
+  int32_t vocab_out;         /* lm_head rows; must be <= vocab_in              */
+  int32_t max_seq;           /* KV capacity in positions                       */
+  int32_t n_experts, top_k, n_shared_experts, expert_hidden; /* n_experts 0 = dense */
+  float rms_eps, rope_base;
+  uint32_t flags;            /* KIE_MODE_*                                     */
+  int32_t n_workgroups;      /* persistent grid size; 0 = one per compute unit */
+  int32_t timeout_ms;        /* barrier watchdog; 0 = 20000                    */
+} kie_config;
+
+typedef struct kie_layer_weights {   /* device pointers, fp16, row-major [out][in] */
+  const void *attn_norm;             /* [d]                                        */
+  const void *wq, *wk, *wv;          /* [H*hd][d], [n_kv*hd][d], [n_kv*hd][d]       */
+  const void *wo;                    /* [d][H*hd]                                  */
+  const void *ffn_norm;              /* [d]                                        */
+  const void *w_gate, *w_up;         /* dense: [ffn_hidden][d]                     */
+  const void *w_down;                /* dense: [d][ffn_hidden]                     */
+  const void *router;                /* MoE: [n_experts][d]                        */
+  const void *e_gate, *e_up;         /* MoE: [n_experts + n_shared][expert_hidden][d]
+                                        (routed experts first, then shared)         */
+  const void *e_down;                /* MoE: [n_experts + n_shared][d][expert_hidden] */
+} kie_layer_weights;
+
+typedef struct kie_weights {
+  const void *tok_emb;               /* [vocab_in][d]                              */
+  const void *final_norm;            /* [d]                                        */
+  const void *lm_head;               /* [vocab_out][d]                             */
+  const kie_layer_weights *layers;   /* host array of n_layers entries; copied     */
+} kie_weights;
+
+typedef struct kie_handle kie_handle;
+
+/* Validates a configuration on the host only (no GPU needed).
+ * KIE_OK, KIE_ERR_INVALID_ARG or KIE_ERR_UNSUPPORTED. */
+int kie_config_check(const kie_config *cfg);
+
+/* Creates a decoder on the current HIP device.  Validates cfg and that every
+ * weight pointer lies in device memory large enough for its shape; allocates
+ * the fp16 KV cache ([L][n_kv][max_seq][hd] for K and for V), activation
+ * scratch, barrier words and the RoPE cos/sin table (built in float64,
+ * rounded to fp32).  `hip_stream` (a hipStream_t, NULL = default stream) is
+ * the stream every later launch of this handle uses.  On success *out owns
+ * all of that memory until kie_destroy. */
+int kie_create(const kie_config *cfg, const kie_weights *w, void *hip_stream,
+               kie_handle **out);
+
+/* Copies `tokens` (host, int32 [n_tokens], n_tokens >= 1) to the device and
+ * runs positions 0..n_tokens-2 through every layer (no lm_head) in one
+ * persistent launch; tokens[n_tokens-1] becomes pending.  Needs a fresh or
+ * reset handle (else KIE_ERR_BAD_STATE); KIE_ERR_TOKEN_RANGE for an id
+ * outside [0, vocab_in); KIE_ERR_CONTEXT_OVERFLOW if n_tokens > max_seq. */
+int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
+
+/* Generates n_steps tokens in one launch.  out_tokens: device int32
+ * [n_steps] (required when n_steps > 0).  out_logits: device fp32
+ * [n_steps][vocab_out] or NULL.  n_steps == 0 is a no-op.
+ * KIE_ERR_CONTEXT_OVERFLOW if position + n_steps > max_seq. */
+int kie_decode(kie_handle *h, int32_t n_steps, int32_t *out_tokens, float *out_logits);
+
+/* Drops the context: position 0, no pending token (KV contents are simply
+ * overwritten by the next prefill).  Also clears a broken state. */
+int kie_reset(kie_handle *h);
+
+/* Next position to be written (P-1 after a prefill of P tokens). */
+int kie_get_position(const kie_handle *h, int32_t *pos);
+
+/* Frees everything the handle owns.  NULL is allowed. */
+void kie_destroy(kie_handle *h);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *kie_last_error(void);
+
+/* Device time of the last kie_prefill/kie_decode launch region of this
+ * handle, in milliseconds (HIP events on the handle's stream). */
+int kie_last_elapsed_ms(const kie_handle *h, float *ms);
+
+/* ---- inspection entry points (used by the parity tests) ---------------- */
+
+/* Copies K and V rows [pos0, pos1) of `layer`, all KV heads, to host
+ * buffers laid out [n_kv][pos1-pos0][head_dim] fp16 (either may be NULL).
+ * K rows are stored after RoPE. */
+int kie_debug_read_kv(const kie_handle *h, int32_t layer, int32_t pos0, int32_t pos1,
+                      void *k_host, void *v_host);
+
+/* MoE only: routed expert ids chosen by the last kie_decode call, host int32
+ * [n_steps][n_layers][top_k] in rank order (largest probability first). */
+int kie_debug_expert_ids(const kie_handle *h, int32_t *ids_host, int32_t n_steps);
+
+/* y = W x with the decode kernel's GEMV stage code: W device fp16 [rows][cols]
+ * row-major (cols a multiple of 8), x device fp32 [cols], y device fp32
+ * [rows].  Synchronous on `hip_stream`.  Runs n_workgroups (0 = one per CU)
+ * workgroups. */
+int kie_debug_gemv(const void *w, const float *x, float *y, int32_t rows, int32_t cols,
+                   int32_t n_workgroups, void *hip_stream);
+
+/* Grid-barrier stress test: n_rounds barriers over n_workgroups persistent
+ * workgroups; each round every workgroup checks that all others reached the
+ * previous round.  Returns KIE_OK, KIE_ERR_TIMEOUT, or KIE_ERR_INVALID_ARG
+ * (*violations receives the number of failed checks).  spin_limit > 0 caps
+ * each wait at that many polls (a host-forced watchdog test). */
+int kie_debug_barrier(int32_t n_workgroups, int32_t n_rounds, int32_t spin_limit,
+                      int32_t *violations, float *ms_per_barrier, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIE_H */

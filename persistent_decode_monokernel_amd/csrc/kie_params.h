@@ -1,0 +1,106 @@
+// Kernel parameter block shared by the host runtime and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kie {
+
+constexpr int kThreads = 512;              // one workgroup per CU: 8 wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxGroup = 4;               // query heads per KV head
+constexpr int kMaxHeadDim = 128;           // 16 lanes x 8 fp16 per K/V row
+constexpr int kMaxActiveExperts = 16;      // top_k + shared
+
+// Status codes written by the device into Params::err (same values as kie_status).
+constexpr int kErrTimeout = -7;
+
+struct LayerPtrs {
+  const __half *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm;
+  const __half *w_gate, *w_up, *w_down;
+  const __half *router, *e_gate, *e_up, *e_down;
+};
+
+enum Mode : int { kPrefill = 0, kDecode = 1 };
+
+struct Params {
+  // ---- shapes
+  int L, d, H, nkv, hd, F, Vin, Vout, cap;
+  int E, topk, nshared, Fe;     // MoE (E == 0: dense)
+  float eps;
+  int n_wg;                     // workgroups in the grid
+  int splits;                   // attention position splits per KV head
+  // ---- weights (caller-owned, fp16)
+  const __half* tok_emb;        // [Vin][d]
+  const __half* final_norm;     // [d]
+  const __half* lm_head;        // [Vout][d]
+  const LayerPtrs* layers;      // device array [L]
+  // ---- library-owned device state
+  __half* kc;                   // [L][nkv][cap][hd]
+  __half* vc;                   // [L][nkv][cap][hd]
+  const float* rope_cos;        // [cap][hd/2]
+  const float* rope_sin;        // [cap][hd/2]
+  float* x;                     // [d]      residual stream
+  float* qkv;                   // [H*hd + 2*nkv*hd]
+  float* o;                     // [H*hd]   attention output (head-major)
+  float* u;                     // [max(F, (topk+nshared)*Fe)]  FFN hidden
+  float* part;                  // [H][splits][hd+2]  split-K partial (acc, m, l)
+  float* router_logits;         // [E]
+  unsigned* bar;                // grid barrier counter
+  unsigned* head_ctr;           // [nkv] split arrivals per KV head
+  unsigned long long* amax;     // [2] packed (logit, index) argmax slots
+  int* err;                     // device error word (0 = ok)
+  int* state;                   // [0] pending token, [1] graph-mode step counter
+  int* expert_log;              // [cap][L][topk] MoE routing record (decode)
+  // ---- per call
+  int mode;                     // kPrefill / kDecode
+  int n_steps;
+  int pos0;                     // position of step 0
+  const int* prompt;            // prefill: tokens [n_steps + 1]
+  int* out_tokens;              // decode: [n_steps]
+  float* out_logits;            // decode: [n_steps][Vout] or nullptr
+  long long timeout_ticks;      // barrier watchdog in wall-clock ticks
+  int spin_limit;               // > 0: cap on polls per wait (forced-watchdog tests)
+};
+
+// Host-visible launchers implemented next to the kernels.
+int max_blocks_per_cu(size_t lds_bytes);
+hipError_t launch_mono(const Params& p, size_t lds_bytes, hipStream_t s);
+hipError_t launch_staged_step(const Params& p, size_t lds_bytes, hipStream_t s);
+hipError_t launch_gemv(const __half* w, const float* x, float* y, int rows, int cols, int n_wg,
+                       hipStream_t s);
+hipError_t launch_barrier_test(unsigned* bar, int* slots, int* violations, int* err, int n_wg,
+                               int rounds, long long timeout_ticks, int spin_limit,
+                               hipStream_t s);
+
+// Dynamic LDS layout (in floats) shared by host and device:
+//   [0, hcap)            GEMV input vector (largest GEMV input length) or the
+//                        attention unit's q / new-KV / per-wave state area
+//   [red_off, total)     small reduction / routing area
+struct LdsLayout {
+  int hcap;
+  int red_off;
+  int total;
+};
+constexpr int kRedFloats = 2 * kWaves + 2 * kMaxActiveExperts + 64;
+
+__host__ __device__ inline LdsLayout lds_layout(const Params& p) {
+  int v = p.d;
+  v = v > p.H * p.hd ? v : p.H * p.hd;
+  const int moe_in = (p.topk + p.nshared) * p.Fe;
+  if (p.E == 0) v = v > p.F ? v : p.F;
+  else v = v > moe_in ? v : moe_in;
+  const int G = p.H / p.nkv;
+  const int gpad = G <= 1 ? 1 : G <= 2 ? 2 : 4;
+  const int attn = gpad * p.hd + 2 * p.hd + kWaves * gpad * (p.hd + 2);
+  v = v > attn ? v : attn;
+  LdsLayout L;
+  L.hcap = (v + 63) & ~63;
+  L.red_off = L.hcap;
+  L.total = L.hcap + kRedFloats;
+  return L;
+}
+
+}  // namespace kie

@@ -1,0 +1,562 @@
+// Host runtime behind include/kie.h: validation, device memory owned by a
+// handle, and the launches of the persistent decode kernel (or of the staged
+// per-kernel fallback).  No C++ exception crosses the C ABI.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kie.h"
+#include "kie_params.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define KIE_HIP(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(KIE_ERR_HIP, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+bool is_mult(long long v, long long m) { return v > 0 && v % m == 0; }
+
+// Checks that [p, p + bytes) lies inside one device allocation and that p is
+// 16-byte aligned (the kernels read weights with 128-bit loads).
+int check_device_range(const void* p, size_t bytes, const char* what) {
+  if (!p) return fail(KIE_ERR_INVALID_ARG, std::string(what) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(KIE_ERR_INVALID_ARG, std::string(what) + " is not 16-byte aligned");
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(KIE_ERR_INVALID_ARG, std::string(what) + " is not a HIP device pointer");
+  }
+  if (attr.type != hipMemoryTypeDevice)
+    return fail(KIE_ERR_INVALID_ARG, std::string(what) + " is not in device memory");
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(KIE_ERR_INVALID_ARG, std::string(what) + ": cannot query its allocation");
+  }
+  const char* b = static_cast<const char*>(base);
+  const char* q = static_cast<const char*>(p);
+  if (q < b || (size_t)(q - b) + bytes > size)
+    return fail(KIE_ERR_INVALID_ARG, std::string(what) + " is smaller than its shape needs");
+  return KIE_OK;
+}
+
+kie::Params shape_params(const kie_config& c) {
+  kie::Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.L = c.n_layers;
+  p.d = c.d_model;
+  p.H = c.n_heads;
+  p.nkv = c.n_kv_heads;
+  p.hd = c.head_dim;
+  p.F = c.n_experts ? 0 : c.ffn_hidden;
+  p.Vin = c.vocab_in;
+  p.Vout = c.vocab_out;
+  p.cap = c.max_seq;
+  p.E = c.n_experts;
+  p.topk = c.n_experts ? c.top_k : 0;
+  p.nshared = c.n_experts ? c.n_shared_experts : 0;
+  p.Fe = c.n_experts ? c.expert_hidden : 0;
+  p.eps = c.rms_eps;
+  return p;
+}
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+
+}  // namespace
+
+struct kie_handle {
+  kie_config cfg{};
+  kie::Params base{};            // shapes, weights and owned buffers (per-call fields unset)
+  hipStream_t stream = nullptr;
+  int device = 0;
+  size_t lds = 0;
+  long long ticks_per_ms = 100000;
+  std::vector<void*> allocs;     // every hipMalloc of this handle
+  kie::LayerPtrs* d_layers = nullptr;
+  int* d_prompt = nullptr;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  float last_ms = 0.f;
+  int pos = 0;
+  bool pending = false;
+  bool broken = false;
+  int last_decode_steps = 0;
+};
+
+namespace {
+
+int dev_alloc(kie_handle* h, size_t bytes, void** out) {
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes < 256 ? 256 : bytes);
+  if (e != hipSuccess)
+    return fail(KIE_ERR_HIP, std::string("hipMalloc(") + std::to_string(bytes) +
+                                 ") failed: " + hipGetErrorString(e));
+  h->allocs.push_back(p);
+  *out = p;
+  return KIE_OK;
+}
+
+void free_handle(kie_handle* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->stream);
+  for (void* p : h->allocs) (void)hipFree(p);
+  if (h->ev0) (void)hipEventDestroy(h->ev0);
+  if (h->ev1) (void)hipEventDestroy(h->ev1);
+  delete h;
+}
+
+// Clears barrier/argmax/error words before a launch (outside any capture).
+int reset_sync_words(kie_handle* h) {
+  const kie::Params& b = h->base;
+  KIE_HIP(hipMemsetAsync(b.bar, 0, sizeof(unsigned), h->stream));
+  KIE_HIP(hipMemsetAsync(b.head_ctr, 0, sizeof(unsigned) * b.nkv, h->stream));
+  KIE_HIP(hipMemsetAsync(b.amax, 0, 2 * sizeof(unsigned long long), h->stream));
+  KIE_HIP(hipMemsetAsync(b.err, 0, sizeof(int), h->stream));
+  KIE_HIP(hipMemsetAsync(b.state + 1, 0, sizeof(int), h->stream));
+  return KIE_OK;
+}
+
+int finish_launch(kie_handle* h) {
+  KIE_HIP(hipEventRecord(h->ev1, h->stream));
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  int err = 0;
+  KIE_HIP(hipMemcpy(&err, h->base.err, sizeof(int), hipMemcpyDeviceToHost));
+  KIE_HIP(hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  if (err != 0) {
+    h->broken = true;
+    if (err == kie::kErrTimeout)
+      return fail(KIE_ERR_TIMEOUT, "a grid barrier wait timed out; the handle needs kie_reset");
+    return fail(KIE_ERR_HIP, "device reported error " + std::to_string(err));
+  }
+  return KIE_OK;
+}
+
+// Runs p.n_steps steps (prefill or decode) in the handle's mode.
+int run_steps(kie_handle* h, kie::Params& p) {
+  int rc = reset_sync_words(h);
+  if (rc) return rc;
+  const bool staged = (h->cfg.flags & KIE_MODE_GRAPH) != 0;
+  if (!staged) {
+    KIE_HIP(hipEventRecord(h->ev0, h->stream));
+    KIE_HIP(kie::launch_mono(p, h->lds, h->stream));
+    return finish_launch(h);
+  }
+  // Staged mode.  Decode: one step's kernels are captured into a hipGraph
+  // once per call and replayed n_steps times; the step counter and pending
+  // token live in device memory, so every replay is the same graph.
+  // Prefill runs the same per-stage kernels without a graph.
+  if (p.mode == kie::kPrefill || p.n_steps == 0) {
+    KIE_HIP(hipEventRecord(h->ev0, h->stream));
+    for (int i = 0; i < p.n_steps; ++i) KIE_HIP(kie::launch_staged_step(p, h->lds, h->stream));
+    if (p.n_steps == 0 && p.mode == kie::kPrefill)
+      KIE_HIP(hipMemcpyAsync(h->base.state, p.prompt, sizeof(int), hipMemcpyDeviceToDevice,
+                             h->stream));
+    return finish_launch(h);
+  }
+  hipStream_t cap_stream = nullptr;
+  KIE_HIP(hipStreamCreateWithFlags(&cap_stream, hipStreamNonBlocking));
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipError_t e = hipStreamBeginCapture(cap_stream, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t le = kie::launch_staged_step(p, h->lds, cap_stream);
+    e = hipStreamEndCapture(cap_stream, &graph);
+    if (e == hipSuccess) e = le;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipEventRecord(h->ev0, h->stream);
+  for (int i = 0; e == hipSuccess && i < p.n_steps; ++i) e = hipGraphLaunch(exec, h->stream);
+  if (e == hipSuccess) {
+    rc = finish_launch(h);                 // synchronises before the graph is freed
+  } else {
+    (void)hipStreamSynchronize(h->stream);
+    rc = fail(KIE_ERR_HIP, std::string("staged decode graph failed: ") + hipGetErrorString(e));
+  }
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(cap_stream);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kie_last_error(void) { return g_err.c_str(); }
+
+int kie_config_check(const kie_config* c) {
+  g_err.clear();
+  if (!c) return fail(KIE_ERR_INVALID_ARG, "config is NULL");
+  if (c->n_layers < 1 || c->n_layers > 4096) return fail(KIE_ERR_INVALID_ARG, "n_layers out of range");
+  if (!is_mult(c->d_model, 8) || c->d_model > 32768)
+    return fail(KIE_ERR_INVALID_ARG, "d_model must be a positive multiple of 8, at most 32768");
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0)
+    return fail(KIE_ERR_INVALID_ARG, "n_heads must be a positive multiple of n_kv_heads");
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4)
+    return fail(KIE_ERR_UNSUPPORTED, "n_heads / n_kv_heads must be 1, 2 or 4");
+  if (!is_mult(c->head_dim, 8) || c->head_dim > kie::kMaxHeadDim)
+    return fail(KIE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and at most 128");
+  if ((long long)c->n_heads * c->head_dim > 32768)
+    return fail(KIE_ERR_INVALID_ARG, "n_heads * head_dim too large");
+  if (c->n_experts == 0) {
+    if (!is_mult(c->ffn_hidden, 8) || c->ffn_hidden > 65536)
+      return fail(KIE_ERR_INVALID_ARG, "ffn_hidden must be a positive multiple of 8");
+  } else {
+    if (c->n_experts < 1 || c->n_experts > 1024) return fail(KIE_ERR_INVALID_ARG, "n_experts out of range");
+    if (c->top_k < 1 || c->top_k > c->n_experts) return fail(KIE_ERR_INVALID_ARG, "top_k out of range");
+    if (c->n_shared_experts < 0) return fail(KIE_ERR_INVALID_ARG, "n_shared_experts < 0");
+    if (c->top_k + c->n_shared_experts > kie::kMaxActiveExperts)
+      return fail(KIE_ERR_UNSUPPORTED, "top_k + n_shared_experts must be at most 16");
+    if (!is_mult(c->expert_hidden, 8)) return fail(KIE_ERR_INVALID_ARG, "expert_hidden must be a positive multiple of 8");
+  }
+  if (c->vocab_in < 1 || c->vocab_out < 1 || c->vocab_out > c->vocab_in)
+    return fail(KIE_ERR_INVALID_ARG, "need 1 <= vocab_out <= vocab_in");
+  if (c->max_seq < 1 || c->max_seq > (1 << 20)) return fail(KIE_ERR_INVALID_ARG, "max_seq out of range");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(KIE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if (!(c->rope_base > 1.f) || !std::isfinite(c->rope_base)) return fail(KIE_ERR_INVALID_ARG, "rope_base must be > 1");
+  if (c->flags & ~KIE_MODE_GRAPH) return fail(KIE_ERR_INVALID_ARG, "unknown flag bits");
+  if (c->n_workgroups < 0 || c->n_workgroups > 4096) return fail(KIE_ERR_INVALID_ARG, "n_workgroups out of range");
+  if (c->timeout_ms < 0) return fail(KIE_ERR_INVALID_ARG, "timeout_ms < 0");
+  kie::Params p = shape_params(*c);
+  const kie::LdsLayout L = kie::lds_layout(p);
+  if ((size_t)L.total * sizeof(float) > kMaxLdsBytes)
+    return fail(KIE_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
+  return KIE_OK;
+}
+
+int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, kie_handle** out) {
+  int rc = kie_config_check(cfg);
+  if (rc) return rc;
+  if (!w || !out) return fail(KIE_ERR_INVALID_ARG, "weights or out is NULL");
+  if (!w->layers) return fail(KIE_ERR_INVALID_ARG, "weights->layers is NULL");
+  const kie_config& c = *cfg;
+  const size_t d = c.d_model, qd = (size_t)c.n_heads * c.head_dim,
+               kd = (size_t)c.n_kv_heads * c.head_dim, hb = sizeof(__half);
+  // ---- weight pointers: device memory, aligned, large enough
+  if ((rc = check_device_range(w->tok_emb, (size_t)c.vocab_in * d * hb, "tok_emb"))) return rc;
+  if ((rc = check_device_range(w->final_norm, d * hb, "final_norm"))) return rc;
+  if ((rc = check_device_range(w->lm_head, (size_t)c.vocab_out * d * hb, "lm_head"))) return rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const kie_layer_weights& lw = w->layers[l];
+    const std::string pre = "layers[" + std::to_string(l) + "].";
+    struct Need { const void* p; size_t bytes; const char* name; };
+    std::vector<Need> need = {{lw.attn_norm, d * hb, "attn_norm"}, {lw.wq, qd * d * hb, "wq"},
+                              {lw.wk, kd * d * hb, "wk"},          {lw.wv, kd * d * hb, "wv"},
+                              {lw.wo, d * qd * hb, "wo"},          {lw.ffn_norm, d * hb, "ffn_norm"}};
+    if (c.n_experts == 0) {
+      const size_t F = c.ffn_hidden;
+      need.push_back({lw.w_gate, F * d * hb, "w_gate"});
+      need.push_back({lw.w_up, F * d * hb, "w_up"});
+      need.push_back({lw.w_down, d * F * hb, "w_down"});
+    } else {
+      const size_t ne = (size_t)c.n_experts + c.n_shared_experts, fe = c.expert_hidden;
+      need.push_back({lw.router, (size_t)c.n_experts * d * hb, "router"});
+      need.push_back({lw.e_gate, ne * fe * d * hb, "e_gate"});
+      need.push_back({lw.e_up, ne * fe * d * hb, "e_up"});
+      need.push_back({lw.e_down, ne * d * fe * hb, "e_down"});
+    }
+    for (const Need& n : need)
+      if ((rc = check_device_range(n.p, n.bytes, (pre + n.name).c_str()))) return rc;
+  }
+
+  kie_handle* h = new (std::nothrow) kie_handle();
+  if (!h) return fail(KIE_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = c;
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  auto bail = [&](int code) {
+    free_handle(h);
+    return code;
+  };
+  if (hipGetDevice(&h->device) != hipSuccess) return bail(fail(KIE_ERR_HIP, "hipGetDevice failed"));
+  int n_cu = 0, clk_khz = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess)
+    return bail(fail(KIE_ERR_HIP, "device attribute query failed"));
+  if (clk_khz > 0) h->ticks_per_ms = clk_khz;
+
+  kie::Params& p = h->base;
+  p = shape_params(c);
+  p.n_wg = c.n_workgroups > 0 ? c.n_workgroups : n_cu;
+  p.splits = std::max(1, p.n_wg / p.nkv);
+  const kie::LdsLayout L = kie::lds_layout(p);
+  h->lds = (size_t)L.total * sizeof(float);
+  const int per_cu = kie::max_blocks_per_cu(h->lds);
+  if (per_cu < 1 || (long long)per_cu * n_cu < p.n_wg)
+    return bail(fail(KIE_ERR_OCCUPANCY, "grid of " + std::to_string(p.n_wg) +
+                                            " workgroups cannot be co-resident (" +
+                                            std::to_string(per_cu) + " per CU x " +
+                                            std::to_string(n_cu) + " CUs)"));
+  p.tok_emb = static_cast<const __half*>(w->tok_emb);
+  p.final_norm = static_cast<const __half*>(w->final_norm);
+  p.lm_head = static_cast<const __half*>(w->lm_head);
+
+  // ---- owned buffers
+  const size_t cap = c.max_seq, hd = c.head_dim;
+  const size_t kv_elems = (size_t)c.n_layers * c.n_kv_heads * cap * hd;
+  void* ptr = nullptr;
+#define KIE_ALLOC(field, type, count)                                   \
+  do {                                                                  \
+    if ((rc = dev_alloc(h, sizeof(type) * (size_t)(count), &ptr))) return bail(rc); \
+    p.field = static_cast<type*>(ptr);                                  \
+  } while (0)
+  KIE_ALLOC(kc, __half, kv_elems);
+  KIE_ALLOC(vc, __half, kv_elems);
+  float* rc_tab = nullptr;
+  if ((rc = dev_alloc(h, sizeof(float) * cap * hd, &ptr))) return bail(rc);
+  rc_tab = static_cast<float*>(ptr);
+  p.rope_cos = rc_tab;
+  p.rope_sin = rc_tab + cap * (hd / 2);
+  KIE_ALLOC(x, float, d);
+  KIE_ALLOC(qkv, float, qd + 2 * kd);
+  KIE_ALLOC(o, float, qd);
+  const size_t ucount = c.n_experts ? (size_t)(c.top_k + c.n_shared_experts) * c.expert_hidden
+                                    : (size_t)c.ffn_hidden;
+  KIE_ALLOC(u, float, ucount);
+  KIE_ALLOC(part, float, (size_t)c.n_heads * p.splits * (hd + 2));
+  KIE_ALLOC(router_logits, float, std::max(1, c.n_experts));
+  KIE_ALLOC(bar, unsigned, 1);
+  KIE_ALLOC(head_ctr, unsigned, c.n_kv_heads);
+  KIE_ALLOC(amax, unsigned long long, 2);
+  KIE_ALLOC(err, int, 1);
+  KIE_ALLOC(state, int, 4);
+  KIE_ALLOC(expert_log, int, c.n_experts ? cap * c.n_layers * c.top_k : 1);
+#undef KIE_ALLOC
+  if ((rc = dev_alloc(h, sizeof(int) * cap, &ptr))) return bail(rc);
+  h->d_prompt = static_cast<int*>(ptr);
+  if ((rc = dev_alloc(h, sizeof(kie::LayerPtrs) * c.n_layers, &ptr))) return bail(rc);
+  h->d_layers = static_cast<kie::LayerPtrs*>(ptr);
+  p.layers = h->d_layers;
+
+  std::vector<kie::LayerPtrs> lp(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const kie_layer_weights& s = w->layers[l];
+    kie::LayerPtrs& t = lp[l];
+    auto hp = [](const void* v) { return static_cast<const __half*>(v); };
+    t.attn_norm = hp(s.attn_norm); t.wq = hp(s.wq); t.wk = hp(s.wk); t.wv = hp(s.wv);
+    t.wo = hp(s.wo); t.ffn_norm = hp(s.ffn_norm);
+    t.w_gate = hp(s.w_gate); t.w_up = hp(s.w_up); t.w_down = hp(s.w_down);
+    t.router = hp(s.router); t.e_gate = hp(s.e_gate); t.e_up = hp(s.e_up); t.e_down = hp(s.e_down);
+  }
+  // RoPE table: angle p * base^(-2j/hd) in float64, cos/sin rounded once to fp32.
+  std::vector<float> tab(cap * hd);
+  const size_t half = hd / 2;
+  for (size_t j = 0; j < half; ++j) {
+    const double theta = std::pow((double)c.rope_base, -2.0 * (double)j / (double)hd);
+    for (size_t q = 0; q < cap; ++q) {
+      const double a = (double)q * theta;
+      tab[q * half + j] = (float)std::cos(a);
+      tab[cap * half + q * half + j] = (float)std::sin(a);
+    }
+  }
+  if (hipMemcpy(h->d_layers, lp.data(), sizeof(kie::LayerPtrs) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(rc_tab, tab.data(), sizeof(float) * tab.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(p.state, 0, 4 * sizeof(int)) != hipSuccess ||
+      hipEventCreate(&h->ev0) != hipSuccess || hipEventCreate(&h->ev1) != hipSuccess)
+    return bail(fail(KIE_ERR_HIP, "initialising handle buffers failed"));
+  const int tmo = c.timeout_ms > 0 ? c.timeout_ms : 20000;
+  p.timeout_ticks = (long long)tmo * h->ticks_per_ms;
+  *out = h;
+  g_err.clear();
+  return KIE_OK;
+}
+
+int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
+  g_err.clear();
+  if (!h || !tokens) return fail(KIE_ERR_INVALID_ARG, "handle or tokens is NULL");
+  if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
+  if (h->pos != 0 || h->pending) return fail(KIE_ERR_BAD_STATE, "prefill needs a fresh or reset handle");
+  if (n < 1) return fail(KIE_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (n > h->cfg.max_seq) return fail(KIE_ERR_CONTEXT_OVERFLOW, "prompt longer than max_seq");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= h->cfg.vocab_in)
+      return fail(KIE_ERR_TOKEN_RANGE, "prompt token " + std::to_string(i) + " out of range");
+  KIE_HIP(hipMemcpyAsync(h->d_prompt, tokens, sizeof(int) * n, hipMemcpyHostToDevice, h->stream));
+  kie::Params p = h->base;
+  p.mode = kie::kPrefill;
+  p.n_steps = n - 1;
+  p.pos0 = 0;
+  p.prompt = h->d_prompt;
+  int rc = run_steps(h, p);
+  if (rc) return rc;
+  h->pos = n - 1;
+  h->pending = true;
+  return KIE_OK;
+}
+
+int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits) {
+  g_err.clear();
+  if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
+  if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
+  if (n < 0) return fail(KIE_ERR_INVALID_ARG, "n_steps < 0");
+  if (n == 0) return KIE_OK;
+  if (!h->pending) return fail(KIE_ERR_BAD_STATE, "decode needs a prompt (kie_prefill)");
+  if ((long long)h->pos + n > h->cfg.max_seq)
+    return fail(KIE_ERR_CONTEXT_OVERFLOW, "position + n_steps exceeds max_seq");
+  int rc = check_device_range(out_tokens, sizeof(int32_t) * (size_t)n, "out_tokens");
+  if (rc) return rc;
+  if (out_logits &&
+      (rc = check_device_range(out_logits, sizeof(float) * (size_t)n * h->cfg.vocab_out, "out_logits")))
+    return rc;
+  kie::Params p = h->base;
+  p.mode = kie::kDecode;
+  p.n_steps = n;
+  p.pos0 = h->pos;
+  p.out_tokens = out_tokens;
+  p.out_logits = out_logits;
+  rc = run_steps(h, p);
+  if (rc) return rc;
+  h->pos += n;
+  h->last_decode_steps = n;
+  return KIE_OK;
+}
+
+int kie_reset(kie_handle* h) {
+  g_err.clear();
+  if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  h->pos = 0;
+  h->pending = false;
+  h->broken = false;
+  h->last_decode_steps = 0;
+  return KIE_OK;
+}
+
+int kie_get_position(const kie_handle* h, int32_t* pos) {
+  if (!h || !pos) return fail(KIE_ERR_INVALID_ARG, "handle or pos is NULL");
+  *pos = h->pos;
+  return KIE_OK;
+}
+
+int kie_last_elapsed_ms(const kie_handle* h, float* ms) {
+  if (!h || !ms) return fail(KIE_ERR_INVALID_ARG, "handle or ms is NULL");
+  *ms = h->last_ms;
+  return KIE_OK;
+}
+
+void kie_destroy(kie_handle* h) { free_handle(h); }
+
+int kie_debug_read_kv(const kie_handle* h, int32_t layer, int32_t pos0, int32_t pos1, void* k_host,
+                      void* v_host) {
+  g_err.clear();
+  if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
+  const kie_config& c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers || pos0 < 0 || pos1 < pos0 || pos1 > c.max_seq)
+    return fail(KIE_ERR_INVALID_ARG, "layer or position range out of bounds");
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  const size_t hd = c.head_dim, cap = c.max_seq, rows = (size_t)(pos1 - pos0);
+  const size_t row_bytes = hd * sizeof(__half);
+  for (int g = 0; g < c.n_kv_heads; ++g) {
+    const size_t src = (((size_t)layer * c.n_kv_heads + g) * cap + pos0) * hd;
+    const size_t dst = (size_t)g * rows * hd;
+    if (k_host && rows)
+      KIE_HIP(hipMemcpy(static_cast<__half*>(k_host) + dst, h->base.kc + src, rows * row_bytes,
+                        hipMemcpyDeviceToHost));
+    if (v_host && rows)
+      KIE_HIP(hipMemcpy(static_cast<__half*>(v_host) + dst, h->base.vc + src, rows * row_bytes,
+                        hipMemcpyDeviceToHost));
+  }
+  return KIE_OK;
+}
+
+int kie_debug_expert_ids(const kie_handle* h, int32_t* ids_host, int32_t n_steps) {
+  g_err.clear();
+  if (!h || !ids_host) return fail(KIE_ERR_INVALID_ARG, "handle or ids is NULL");
+  const kie_config& c = h->cfg;
+  if (c.n_experts == 0) return fail(KIE_ERR_INVALID_ARG, "not a MoE model");
+  if (n_steps < 0 || n_steps > h->last_decode_steps)
+    return fail(KIE_ERR_INVALID_ARG, "n_steps exceeds the last decode call");
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  if (n_steps)
+    KIE_HIP(hipMemcpy(ids_host, h->base.expert_log,
+                      sizeof(int) * (size_t)n_steps * c.n_layers * c.top_k, hipMemcpyDeviceToHost));
+  return KIE_OK;
+}
+
+int kie_debug_gemv(const void* w, const float* x, float* y, int32_t rows, int32_t cols,
+                   int32_t n_wg, void* hip_stream) {
+  g_err.clear();
+  if (rows < 1 || !is_mult(cols, 8) || cols > 16384)
+    return fail(KIE_ERR_INVALID_ARG, "need rows >= 1 and cols a multiple of 8, at most 16384");
+  int rc;
+  if ((rc = check_device_range(w, (size_t)rows * cols * sizeof(__half), "w"))) return rc;
+  if ((rc = check_device_range(x, (size_t)cols * sizeof(float), "x"))) return rc;
+  if ((rc = check_device_range(y, (size_t)rows * sizeof(float), "y"))) return rc;
+  int dev = 0, n_cu = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  KIE_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (n_wg < 0 || n_wg > 65536) return fail(KIE_ERR_INVALID_ARG, "n_workgroups out of range");
+  const int grid = n_wg > 0 ? n_wg : n_cu;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  KIE_HIP(kie::launch_gemv(static_cast<const __half*>(w), x, y, rows, cols, grid, s));
+  KIE_HIP(hipStreamSynchronize(s));
+  return KIE_OK;
+}
+
+int kie_debug_barrier(int32_t n_wg, int32_t rounds, int32_t spin_limit, int32_t* violations,
+                      float* ms_per_barrier, void* hip_stream) {
+  g_err.clear();
+  if (!violations || rounds < 1 || rounds > 1000000 || spin_limit < 0)
+    return fail(KIE_ERR_INVALID_ARG, "bad barrier test arguments");
+  int dev = 0, n_cu = 0, clk = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  KIE_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  KIE_HIP(hipDeviceGetAttribute(&clk, hipDeviceAttributeWallClockRate, dev));
+  const int grid = n_wg > 0 ? n_wg : n_cu;
+  if (grid > n_cu) return fail(KIE_ERR_OCCUPANCY, "barrier test runs one workgroup per CU at most");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* mem = nullptr;
+  const size_t bytes = 64 + sizeof(int) * (size_t)grid;
+  KIE_HIP(hipMalloc(&mem, bytes));
+  int rc = KIE_OK;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  unsigned* bar = static_cast<unsigned*>(mem);
+  int* viol = reinterpret_cast<int*>(static_cast<char*>(mem) + 16);
+  int* err = reinterpret_cast<int*>(static_cast<char*>(mem) + 32);
+  int* slots = reinterpret_cast<int*>(static_cast<char*>(mem) + 64);
+  do {
+    if (hipMemsetAsync(mem, 0, bytes, s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
+        hipEventCreate(&e1) != hipSuccess || hipEventRecord(e0, s) != hipSuccess) {
+      rc = fail(KIE_ERR_HIP, "barrier test setup failed");
+      break;
+    }
+    const long long ticks = 5000LL * (clk > 0 ? clk : 100000);
+    hipError_t e = kie::launch_barrier_test(bar, slots, viol, err, grid, rounds, ticks, spin_limit, s);
+    if (e != hipSuccess) {
+      rc = fail(KIE_ERR_HIP, std::string("barrier test launch: ") + hipGetErrorString(e));
+      break;
+    }
+    int host[2] = {0, 0};
+    float ms = 0.f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess ||
+        hipMemcpy(&host[0], viol, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(&host[1], err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      rc = fail(KIE_ERR_HIP, "barrier test readback failed");
+      break;
+    }
+    *violations = host[0];
+    if (ms_per_barrier) *ms_per_barrier = ms / (2.0f * rounds);
+    if (host[1] == kie::kErrTimeout) rc = fail(KIE_ERR_TIMEOUT, "barrier wait timed out");
+  } while (0);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(mem);
+  return rc;
+}
+
+}  // extern "C"

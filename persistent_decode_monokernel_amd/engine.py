@@ -1,0 +1,163 @@
+"""Python face of libkie.so: the same calls as include/kie.h, with torch used
+only to hold device memory and to name the stream.  Every step of decode
+runs in the library's HIP kernels; nothing here computes."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import Config, KieError, LayerWeights, Weights, check
+
+_CFG_FIELDS = ("n_layers", "d_model", "n_heads", "n_kv_heads", "head_dim", "ffn_hidden",
+               "vocab_in", "vocab_out", "n_experts", "top_k", "n_shared_experts",
+               "expert_hidden", "rms_eps", "rope_base")
+
+
+def make_config(model, max_seq: Optional[int] = None, graph: bool = False,
+                n_workgroups: int = 0, timeout_ms: int = 0) -> Config:
+    """kie_config from any object with the model-shape attributes."""
+    c = Config()
+    for f in _CFG_FIELDS:
+        setattr(c, f, getattr(model, f))
+    if max_seq is None:
+        max_seq = getattr(model, "kv_capacity")
+    c.max_seq = int(max_seq)
+    c.flags = _lib.KIE_MODE_GRAPH if graph else 0
+    c.n_workgroups = int(n_workgroups)
+    c.timeout_ms = int(timeout_ms)
+    return c
+
+
+def config_check(model, **kw) -> None:
+    lib = _lib.load()
+    c = make_config(model, **kw)
+    check(lib.kie_config_check(ctypes.byref(c)), "kie_config_check")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != torch.float16 or not t.is_contiguous():
+        raise ValueError("weights must be contiguous fp16 CUDA tensors")
+    return t.data_ptr()
+
+
+class Engine:
+    """One decoder handle (kie_create .. kie_destroy)."""
+
+    def __init__(self, model, weights: dict, max_seq: Optional[int] = None, graph: bool = False,
+                 n_workgroups: int = 0, timeout_ms: int = 0, stream: Optional[torch.cuda.Stream] = None):
+        self.lib = _lib.load()
+        self.model = model
+        self.cfg = make_config(model, max_seq, graph, n_workgroups, timeout_ms)
+        self._weights = weights                       # keep the device memory alive
+        L = model.n_layers
+        self._layers = (LayerWeights * L)()
+        for l, lw in enumerate(weights["layers"]):
+            for name in LayerWeights._fields_:
+                key = name[0]
+                if key in lw:
+                    setattr(self._layers[l], key, _ptr(lw[key]))
+        self._w = Weights(_ptr(weights["tok_emb"]), _ptr(weights["final_norm"]),
+                          _ptr(weights["lm_head"]), self._layers)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        h = ctypes.c_void_p()
+        check(self.lib.kie_create(ctypes.byref(self.cfg), ctypes.byref(self._w),
+                                  ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h)),
+              "kie_create")
+        self.h = h
+
+    # ---- calls -------------------------------------------------------------
+    def prefill(self, tokens: Sequence[int]) -> None:
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        check(self.lib.kie_prefill(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   int(t.size)), "kie_prefill")
+
+    def decode_into(self, n: int, out_tokens: Optional[torch.Tensor],
+                    out_logits: Optional[torch.Tensor] = None) -> None:
+        tp = out_tokens.data_ptr() if out_tokens is not None else None
+        lp = out_logits.data_ptr() if out_logits is not None else None
+        check(self.lib.kie_decode(self.h, int(n), tp, lp), "kie_decode")
+
+    def decode(self, n: int, logits: bool = True):
+        dev = self._weights["tok_emb"].device
+        toks = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        lg = torch.empty((max(n, 1), self.model.vocab_out), dtype=torch.float32, device=dev) if logits else None
+        self.decode_into(n, toks, lg)
+        return toks[:n], (lg[:n] if lg is not None else None)
+
+    def reset(self) -> None:
+        check(self.lib.kie_reset(self.h), "kie_reset")
+
+    @property
+    def position(self) -> int:
+        p = ctypes.c_int32()
+        check(self.lib.kie_get_position(self.h, ctypes.byref(p)), "kie_get_position")
+        return p.value
+
+    def last_elapsed_ms(self) -> float:
+        ms = ctypes.c_float()
+        check(self.lib.kie_last_elapsed_ms(self.h, ctypes.byref(ms)), "kie_last_elapsed_ms")
+        return ms.value
+
+    def read_kv(self, layer: int, pos0: int, pos1: int):
+        m = self.model
+        shape = (m.n_kv_heads, pos1 - pos0, m.head_dim)
+        k = np.empty(shape, np.float16)
+        v = np.empty(shape, np.float16)
+        check(self.lib.kie_debug_read_kv(self.h, layer, pos0, pos1, k.ctypes.data, v.ctypes.data),
+              "kie_debug_read_kv")
+        return k, v
+
+    def expert_ids(self, n_steps: int) -> np.ndarray:
+        m = self.model
+        ids = np.empty((n_steps, m.n_layers, m.top_k), np.int32)
+        check(self.lib.kie_debug_expert_ids(self.h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                            n_steps), "kie_debug_expert_ids")
+        return ids
+
+    def close(self) -> None:
+        if getattr(self, "h", None) is not None and self.h.value:
+            self.lib.kie_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def debug_gemv(w: torch.Tensor, x: torch.Tensor, n_workgroups: int = 0) -> torch.Tensor:
+    """y = w x through the decode kernel's GEMV stage code (w fp16 [rows][cols], x fp32)."""
+    lib = _lib.load()
+    rows, cols = w.shape
+    y = torch.empty(rows, dtype=torch.float32, device=w.device)
+    s = torch.cuda.current_stream()
+    check(lib.kie_debug_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), rows, cols, n_workgroups,
+                             ctypes.c_void_p(s.cuda_stream)), "kie_debug_gemv")
+    return y
+
+
+def debug_barrier(n_workgroups: int = 0, rounds: int = 1000, spin_limit: int = 0):
+    """Grid-barrier stress: returns (violations, ms per barrier)."""
+    lib = _lib.load()
+    v = ctypes.c_int32()
+    ms = ctypes.c_float()
+    s = torch.cuda.current_stream()
+    check(lib.kie_debug_barrier(n_workgroups, rounds, spin_limit, ctypes.byref(v), ctypes.byref(ms),
+                                ctypes.c_void_p(s.cuda_stream)), "kie_debug_barrier")
+    return v.value, ms.value
+
+
+__all__ = ["Engine", "KieError", "make_config", "config_check", "debug_gemv", "debug_barrier"]

@@ -1,0 +1,50 @@
+"""Teacher-forced comparison of GPU decode output with the oracle.
+
+Tolerances (the workload's stated bar): per step, max |z_gpu - z_oracle| is
+at most 2e-2 and at most 1e-2 of the oracle's logit range for that step;
+the greedy token must equal the oracle's argmax wherever the oracle's
+top-2 margin exceeds 5e-2; token ids and positions are exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ABS_TOL = 2e-2
+REL_RANGE_TOL = 1e-2
+MARGIN = 5e-2
+
+
+def compare_steps(z_gpu: np.ndarray, tok_gpu: np.ndarray, z_or: np.ndarray, skip=()):
+    """Returns a report dict; raises AssertionError on the first failing step."""
+    n = len(tok_gpu)
+    pinned = unpinned = 0
+    worst = 0.0
+    for i in range(n):
+        if i in skip:
+            continue
+        zo = z_or[i].astype(np.float64)
+        zg = z_gpu[i].astype(np.float64)
+        err = float(np.max(np.abs(zg - zo)))
+        rng = float(zo.max() - zo.min())
+        worst = max(worst, err)
+        assert err <= ABS_TOL, f"step {i}: max |dz| = {err:.3e} > {ABS_TOL}"
+        assert err <= REL_RANGE_TOL * rng, f"step {i}: max |dz| = {err:.3e} > 1e-2 * range {rng:.3f}"
+        top2 = np.partition(zo, -2)[-2:]
+        margin = float(top2[1] - top2[0])
+        if margin > MARGIN:
+            pinned += 1
+            assert int(tok_gpu[i]) == int(np.argmax(zo)), (
+                f"step {i}: gpu token {int(tok_gpu[i])} != oracle argmax {int(np.argmax(zo))} "
+                f"(margin {margin:.3f})")
+        else:
+            unpinned += 1
+    return {"steps": n, "pinned": pinned, "unpinned": unpinned, "worst_abs": worst}
+
+
+def kv_close(k_gpu_f16: np.ndarray, k_or: np.ndarray, what: str):
+    """fp16-rounded cache rows vs the oracle's fp32 rows: 2e-3 * max(1, |x|)."""
+    g = k_gpu_f16.astype(np.float64)
+    o = k_or.astype(np.float64)
+    tol = 2e-3 * np.maximum(1.0, np.abs(o))
+    bad = np.abs(g - o) > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} KV elements off, worst {float(np.max(np.abs(g - o))):.3e}"

@@ -1,0 +1,97 @@
+"""C-ABI checks that need no GPU: libkie.so loads, exports every function
+include/kie.h declares, and validates configurations on the host."""
+import ctypes
+
+import pytest
+
+import persistent_decode_monokernel_amd as kie
+from persistent_decode_monokernel_amd import _lib
+from persistent_decode_monokernel_amd.engine import make_config
+from kie_synth import PRESETS
+
+
+def test_header_declares_the_boundary():
+    names = _lib.declared_functions()
+    for must in ("kie_create", "kie_prefill", "kie_decode", "kie_reset", "kie_destroy",
+                 "kie_last_error", "kie_config_check", "kie_get_position"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    missing = [n for n in _lib.declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("name", sorted(PRESETS))
+def test_presets_pass_host_validation(name):
+    kie.config_check(PRESETS[name])
+
+
+def _code(model, **kw):
+    lib = _lib.load()
+    c = make_config(model, **kw)
+    for k, v in kw.pop("fields", {}).items():
+        setattr(c, k, v)
+    return lib.kie_config_check(ctypes.byref(c)), lib.kie_last_error().decode()
+
+
+def _with(model, **fields):
+    lib = _lib.load()
+    c = make_config(model)
+    for k, v in fields.items():
+        setattr(c, k, v)
+    rc = lib.kie_config_check(ctypes.byref(c))
+    return rc, lib.kie_last_error().decode()
+
+
+@pytest.mark.parametrize("fields,code", [
+    ({"d_model": 100}, -1),                      # not a multiple of 8
+    ({"n_heads": 6, "n_kv_heads": 4}, -1),       # heads not a multiple of kv heads
+    ({"n_heads": 24, "n_kv_heads": 3}, -8),      # group of 8 not implemented
+    ({"head_dim": 192}, -8),                     # wider than 16 lanes x 8
+    ({"head_dim": 60}, -8),                      # not a multiple of 8
+    ({"ffn_hidden": 1000 + 4}, -1),
+    ({"vocab_out": 5000}, -1),                   # lm_head rows > embedding rows
+    ({"max_seq": 0}, -1),
+    ({"rms_eps": -1.0}, -1),
+    ({"rope_base": 1.0}, -1),
+    ({"flags": 0x80}, -1),
+    ({"n_workgroups": -3}, -1),
+    ({"timeout_ms": -1}, -1),
+])
+def test_invalid_configs_are_rejected(fields, code):
+    rc, msg = _with(PRESETS["tiny"], **fields)
+    assert rc == code, (rc, msg)
+    assert msg
+
+
+def test_moe_field_validation():
+    m = PRESETS["moe"]
+    assert _with(m, top_k=0)[0] == -1
+    assert _with(m, top_k=65)[0] == -1
+    assert _with(m, top_k=15, n_shared_experts=2)[0] == -8    # more than 16 active experts
+    assert _with(m, expert_hidden=1404)[0] == -1
+
+
+def test_lds_budget_rejects_huge_ffn():
+    rc, msg = _with(PRESETS["tiny"], ffn_hidden=65536)
+    assert rc == -8 and "LDS" in msg
+
+
+def test_null_config_and_last_error():
+    lib = _lib.load()
+    assert lib.kie_config_check(None) == -1
+    assert b"NULL" in lib.kie_last_error()
+    assert lib.kie_config_check(ctypes.byref(make_config(PRESETS["2b"]))) == 0
+    assert lib.kie_last_error() == b""
+
+
+def test_null_handle_calls_are_rejected():
+    lib = _lib.load()
+    assert lib.kie_prefill(None, None, 1) == -1
+    assert lib.kie_decode(None, 1, None, None) == -1
+    assert lib.kie_reset(None) == -1
+    p = ctypes.c_int32()
+    assert lib.kie_get_position(None, ctypes.byref(p)) == -1
+    lib.kie_destroy(None)                       # allowed

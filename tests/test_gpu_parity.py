@@ -1,0 +1,217 @@
+"""GPU parity: the HIP decode path (through the C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (fp16 weights ~ N(0, 0.02), uniform
+prompt ids); the oracle reads host copies of the same fp16 bytes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from kie_synth import get_config, make_prompt, make_weights, weights_to_numpy
+from oracle import Oracle
+from tests.parity import compare_steps, kv_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.fixture(scope="module")
+def kie():
+    import persistent_decode_monokernel_amd as k
+    k.load()
+    return k
+
+
+def _model(name, **kw):
+    return get_config(name, **kw)
+
+
+def _gpu_weights(torch, cfg, seed=0):
+    return make_weights(cfg, seed=seed, device="cuda")
+
+
+# ------------------------------------------------------------------- GEMV
+@pytest.mark.parametrize("rows,cols", [(7680, 2560), (6912, 2560), (2560, 6912), (32768, 2560),
+                                       (2560, 384), (2560, 864), (100, 72), (3, 8), (513, 1032)])
+def test_gemv_stage_matches_float64(torch, kie, rows, cols):
+    _say("gemv", rows, cols)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(rows * 7 + cols)
+    w = (torch.randn(rows, cols, generator=g, device="cuda") * 0.02).half()
+    x = torch.randn(cols, generator=g, device="cuda")
+    for n_wg in (0, 7):
+        y = kie.debug_gemv(w, x, n_workgroups=n_wg).cpu().numpy().astype(np.float64)
+        wn = w.cpu().numpy().astype(np.float64)
+        xn = x.cpu().numpy().astype(np.float64)
+        want = wn @ xn
+        scale = np.abs(wn) @ np.abs(xn)
+        assert np.all(np.abs(y - want) <= 1e-5 * scale + 1e-30), float(np.max(np.abs(y - want) / scale))
+
+
+# ---------------------------------------------------------------- barrier
+def test_grid_barrier_stress(torch, kie):
+    _say("barrier stress")
+    viol, ms = kie.debug_barrier(0, rounds=2000)
+    _say(f"barrier: {ms * 1e3:.2f} us per barrier")
+    assert viol == 0
+
+
+def test_grid_barrier_watchdog_forced_from_host(torch, kie):
+    # a spin limit of 1 poll makes waits give up at once: the kernel must
+    # report a timeout and every workgroup must leave normally
+    _say("barrier watchdog")
+    with pytest.raises(kie.KieError) as ei:
+        kie.debug_barrier(0, rounds=50, spin_limit=1)
+    assert ei.value.status == "KIE_ERR_TIMEOUT"
+    viol, _ = kie.debug_barrier(0, rounds=10)      # the GPU is still fine
+    assert viol == 0
+
+
+# ------------------------------------------------------ end-to-end, tiny
+def _run_gpu(torch, kie, cfg, W, prompt, n, **kw):
+    eng = kie.Engine(cfg, W, **kw)
+    eng.prefill(prompt)
+    toks, logits = eng.decode(n)
+    torch.cuda.synchronize()
+    return eng, toks.cpu().numpy(), logits.cpu().numpy()
+
+
+def _oracle_replay(cfg, Wn, prompt, toks):
+    o = Oracle(cfg, Wn)
+    o.prefill(prompt)
+    _, z = o.decode(len(toks), force=toks)
+    return o, z
+
+
+@pytest.mark.parametrize("mode", ["persistent", "graph", "persistent_7wg", "graph_5wg"])
+def test_tiny_decode_parity(torch, kie, mode):
+    cfg = _model("tiny")
+    _say("tiny parity", mode)
+    W = _gpu_weights(torch, cfg)
+    Wn = weights_to_numpy(W)
+    prompt = make_prompt(cfg)
+    kw = {"graph": mode.startswith("graph")}
+    if "_" in mode:
+        kw["n_workgroups"] = int(mode.split("_")[1].rstrip("wg"))
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, cfg.n_decode, **kw)
+    assert eng.position == len(prompt) - 1 + cfg.n_decode
+    o, zo = _oracle_replay(cfg, Wn, prompt, toks)
+    rep = compare_steps(z, toks, zo)
+    _say(mode, rep)
+    assert rep["pinned"] >= cfg.n_decode // 2
+    # KV cache rows (after RoPE for K) at every written position
+    P = len(prompt)
+    for l in range(cfg.n_layers):
+        k, v = eng.read_kv(l, 0, P - 1 + cfg.n_decode)
+        kv_close(k, o.K[l][:, :P - 1 + cfg.n_decode], f"K layer {l}")
+        kv_close(v, o.V[l][:, :P - 1 + cfg.n_decode], f"V layer {l}")
+    eng.close()
+
+
+def test_tiny_determinism_and_composability(torch, kie):
+    cfg = _model("tiny")
+    _say("tiny determinism")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    _, t1, z1 = _run_gpu(torch, kie, cfg, W, prompt, 40)
+    _, t2, z2 = _run_gpu(torch, kie, cfg, W, prompt, 40)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(z1, z2)
+    eng = kie.Engine(cfg, W)
+    eng.prefill(prompt)
+    ta, za = eng.decode(15)
+    tb, zb = eng.decode(25)
+    np.testing.assert_array_equal(np.concatenate([ta.cpu().numpy(), tb.cpu().numpy()]), t1)
+    np.testing.assert_array_equal(np.concatenate([za.cpu().numpy(), zb.cpu().numpy()]), z1)
+    # the staged (graph) mode runs the same stage code: identical bits
+    _, tg, zg = _run_gpu(torch, kie, cfg, W, prompt, 40, graph=True)
+    np.testing.assert_array_equal(tg, t1)
+    np.testing.assert_array_equal(zg, z1)
+    # reset then the same prompt again reproduces the run
+    eng.reset()
+    eng.prefill(prompt)
+    tc, zc = eng.decode(40)
+    np.testing.assert_array_equal(tc.cpu().numpy(), t1)
+    eng.close()
+
+
+def test_tiny_edge_cases(torch, kie):
+    cfg = _model("tiny")
+    _say("tiny edges")
+    W = _gpu_weights(torch, cfg)
+    Wn = weights_to_numpy(W)
+    # a one-token prompt (nothing to prefill) and the last position of the cache
+    prompt = make_prompt(cfg, length=1)
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, 5, max_seq=5)
+    o, zo = _oracle_replay(cfg.with_(max_seq=5), Wn, prompt, toks)
+    compare_steps(z, toks, zo)
+    with pytest.raises(kie.KieError) as ei:
+        eng.decode(1)
+    assert ei.value.status == "KIE_ERR_CONTEXT_OVERFLOW"
+    with pytest.raises(kie.KieError) as ei:
+        eng.prefill(prompt)
+    assert ei.value.status == "KIE_ERR_BAD_STATE"
+    eng.reset()
+    with pytest.raises(kie.KieError) as ei:
+        eng.prefill([cfg.vocab_in])
+    assert ei.value.status == "KIE_ERR_TOKEN_RANGE"
+    with pytest.raises(kie.KieError) as ei:
+        eng.decode(1)
+    assert ei.value.status == "KIE_ERR_BAD_STATE"
+    toks0, _ = eng.decode(0)                  # no-op
+    assert toks0.numel() == 0
+    # a host pointer is refused before any launch
+    import torch as t
+    with pytest.raises(kie.KieError) as ei:
+        eng.prefill(prompt)
+        eng.decode_into(1, t.empty(1, dtype=t.int32))
+    assert ei.value.status == "KIE_ERR_INVALID_ARG"
+    eng.close()
+
+
+def test_tiny_weights_too_small_rejected(torch, kie):
+    cfg = _model("tiny")
+    W = _gpu_weights(torch, cfg)
+    W["lm_head"] = W["lm_head"][: cfg.vocab_out // 2].clone()
+    with pytest.raises(kie.KieError) as ei:
+        kie.Engine(cfg, W)
+    assert ei.value.status == "KIE_ERR_INVALID_ARG"
+
+
+# ------------------------------------------------------ end-to-end, 2.2B
+def test_2b_full_size_parity_sampled(torch, kie):
+    """The ~2.2B model at full size and in the launch shape the benchmark
+    times: prompt 512, then decode; the first 6 steps are replayed by the
+    oracle (teacher forced), and every layer's K/V rows at sampled
+    positions are checked."""
+    cfg = _model("2b")
+    _say("2b parity: weights")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    n = 6
+    _say("2b parity: gpu run")
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n)
+    _say("2b parity: oracle replay")
+    Wn = weights_to_numpy(W)
+    o, zo = _oracle_replay(cfg, Wn, prompt, toks)
+    rep = compare_steps(z, toks, zo)
+    _say("2b", rep)
+    P = len(prompt)
+    for l in (0, 12, 24):
+        for p0 in (0, 255, P - 2, P - 1 + n - 1):
+            k, v = eng.read_kv(l, p0, p0 + 1)
+            kv_close(k, o.K[l][:, p0:p0 + 1], f"K l{l} p{p0}")
+            kv_close(v, o.V[l][:, p0:p0 + 1], f"V l{l} p{p0}")
+    eng.close()
