@@ -83,6 +83,59 @@ def cpu_baseline(cfg, W, prompt, budget_s: float):
             "ms_per_token": 1e3 * el / n}
 
 
+def trace_summary(cfg, tr):
+    """Per-stage timing of one traced decode step from the in-kernel barrier
+    stamps (100 MHz wall clock): for each stage kind, the mean over layers of
+    the mean and the max over workgroups of the time from leaving the
+    previous barrier to arriving at the next, and of the time spent waiting
+    in the barrier."""
+    import numpy as np
+    t = tr.astype(np.float64) * 10.0 / 1000.0          # ticks of 10 ns -> us
+    t -= t[:, :1]
+    kinds = (["qkv", "attn", "o", "router", "gateup", "down"] if cfg.n_experts
+             else ["qkv", "attn", "o", "gateup", "down"])
+    names = [f"{k}" for _ in range(cfg.n_layers) for k in kinds] + ["lm_head"]
+    nb = (t.shape[1] - 1) // 2
+    out = {}
+    prev_leave = t[:, 0]
+    for k in range(min(nb, len(names))):
+        arrive, leave = t[:, 1 + 2 * k], t[:, 2 + 2 * k]
+        work = arrive - prev_leave
+        wait = leave - arrive
+        d = out.setdefault(names[k], {"n": 0, "work_mean_us": 0.0, "work_max_us": 0.0,
+                                      "wait_mean_us": 0.0, "span_us": 0.0})
+        d["n"] += 1
+        d["work_mean_us"] += float(work.mean())
+        d["work_max_us"] += float(work.max())
+        d["wait_mean_us"] += float(wait.mean())
+        d["span_us"] += float(leave.max() - prev_leave.min())
+        prev_leave = leave
+    for d in out.values():
+        for key in ("work_mean_us", "work_max_us", "wait_mean_us", "span_us"):
+            d[key] /= d["n"]
+    return {"step_us": float(t[:, -1].max()), "stages": out}
+
+
+def hbm_probes(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Achievable HBM streaming rates on this device, from the library's
+    plain streaming kernel: a read-only pass over ``read_bytes`` and a copy
+    of ``copy_bytes`` (reads + writes counted)."""
+    import torch
+    import persistent_decode_monokernel_amd as kie
+    src = torch.empty(read_bytes // 2, dtype=torch.float16, device="cuda")
+    src.fill_(1.0)
+    kie.debug_stream(src, None, reps=2)
+    ms_r = kie.debug_stream(src, None, reps=reps)
+    a = src[: copy_bytes // 2]
+    dst = torch.empty_like(a)
+    kie.debug_stream(a, dst, reps=2)
+    ms_c = kie.debug_stream(a, dst, reps=reps)
+    del src, dst
+    return {"read_gbs": read_bytes / (ms_r * 1e-3) / 1e9, "read_bytes": read_bytes,
+            "copy_gbs": 2 * copy_bytes / (ms_c * 1e-3) / 1e9, "copy_bytes": copy_bytes,
+            "read_ms": ms_r, "copy_ms": ms_c, "kernel": "kie::stream_kernel"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +146,13 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=3, help="timed repetitions (median reported)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming probes")
+    ap.add_argument("--trace", action="store_true",
+                    help="also run one traced decode and add a per-stage breakdown to detail")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="launch the persistent kernel with an ordinary dispatch")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="run only the HBM read/copy probes (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -106,6 +166,11 @@ def main(argv=None):
     import persistent_decode_monokernel_amd as kie
     from kie_synth import get_config, make_prompt, make_weights
 
+    if args.probe_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"probe": hbm_probes()}), flush=True)
+        return 0
+
     cfg = get_config(args.config)
     K = args.steps if args.steps is not None else cfg.n_decode
     P = cfg.prompt_len
@@ -116,7 +181,7 @@ def main(argv=None):
     prompt = make_prompt(cfg, seed=0)
     stream = torch.cuda.current_stream()
 
-    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph)
+    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph, plain_launch=args.plain_launch)
     eng.prefill(prompt)
     if args.warmup:
         eng.decode(args.warmup, logits=False)
@@ -141,6 +206,14 @@ def main(argv=None):
     nbytes = decode_bytes(cfg, P - 1, K)
     achieved = nbytes / (kms / 1e3) / 1e9
     eng.close()
+    trace = None
+    if args.trace and not args.graph:
+        te = kie.Engine(cfg, W, max_seq=max_seq, trace=True, plain_launch=args.plain_launch)
+        te.prefill(prompt)
+        te.decode_into(min(K, 8), toks, None)
+        trace = trace_summary(cfg, te.read_trace())
+        te.close()
+    probes = None if args.no_probe else hbm_probes()
 
     out = {
         "metric": METRIC,
@@ -169,7 +242,10 @@ def main(argv=None):
         "detail": {"kernel": "kie::mono_kernel" if not args.graph else "kie::stage_kernel",
                    "bytes_per_launch": nbytes, "bytes_per_token": nbytes / K,
                    "kernel_ms": kms, "call_ms": ms, "reps_call_ms": times,
-                   "roofline_tok_s": HBM_PEAK_GBS * 1e9 / (nbytes / K)},
+                   "roofline_tok_s": HBM_PEAK_GBS * 1e9 / (nbytes / K),
+                   "hbm_probe": probes,
+                   "frac_of_read_probe": (achieved / probes["read_gbs"]) if probes else None,
+                   "trace": trace},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -73,6 +73,21 @@ typedef enum kie_status {
                                  kernels (one kernel per stage) instead of one
                                  persistent launch; same stage code, same
                                  results bit for bit */
+#define KIE_TRACE 0x2u        /* persistent mode: record, for one decode step
+                                 of every kie_decode call (step 1, or step 0
+                                 of a one-step call), each workgroup's clock
+                                 (100 MHz wall clock) when it arrives at and
+                                 leaves every grid barrier; read it back with
+                                 kie_debug_read_trace.  Results are unchanged. */
+#define KIE_PLAIN_LAUNCH 0x4u /* persistent mode: launch with an ordinary
+                                 dispatch instead of the cooperative-launch API
+                                 (for tools that do not follow cooperative
+                                 launches).  Co-residency then rests on the
+                                 occupancy check kie_create makes (one
+                                 workgroup per compute unit fits) and on an
+                                 otherwise idle device; if it is not met, the
+                                 barrier watchdog ends the call with
+                                 KIE_ERR_TIMEOUT instead of hanging. */
 
 typedef struct kie_config {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden;
@@ -178,6 +193,27 @@ int kie_debug_gemv(const void *w, const float *x, float *y, int32_t rows, int32_
  * each wait at that many polls (a host-forced watchdog test). */
 int kie_debug_barrier(int32_t n_workgroups, int32_t n_rounds, int32_t spin_limit,
                       int32_t *violations, float *ms_per_barrier, void *hip_stream);
+
+/* KIE_TRACE handles: copies the trace of the last kie_decode call to
+ * `out` (host, uint64 [n_workgroups][max_events]) and sets *n_events to the
+ * number of events each workgroup recorded: event 0 is the start of the
+ * traced step, then for every grid barrier of that step one event when the
+ * workgroup arrives and one when it leaves.  KIE_ERR_BAD_STATE without
+ * KIE_TRACE or before a decode call; KIE_ERR_INVALID_ARG if max_events is
+ * smaller than the recorded count. */
+int kie_debug_read_trace(const kie_handle *h, uint64_t *out, int32_t max_events,
+                         int32_t *n_events, int32_t *n_workgroups);
+
+/* HBM streaming probe: reads `bytes` (a multiple of 16) from device buffer
+ * `src` with 128-bit non-temporal loads, grid-stride over n_workgroups
+ * workgroups (0 = four per compute unit), and copies them to `dst` when it
+ * is not NULL (same size, device memory, no overlap).  Launched `reps`
+ * times back to back on `hip_stream`; *ms_per_launch receives the average
+ * time of one launch.  Measures the device's achievable streaming
+ * bandwidth, and gives a copy of known size against which memory counters
+ * are calibrated. */
+int kie_debug_stream(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
+                     int32_t reps, float *ms_per_launch, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ STATUS = {
     -6: "KIE_ERR_HIP", -7: "KIE_ERR_TIMEOUT", -8: "KIE_ERR_UNSUPPORTED",
 }
 KIE_MODE_GRAPH = 0x1
+KIE_TRACE = 0x2
+KIE_PLAIN_LAUNCH = 0x4
 
 
 class KieError(RuntimeError):
@@ -79,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_debug_expert_ids": (ctypes.c_int, [VP, P(I32), I32]),
         "kie_debug_gemv": (ctypes.c_int, [VP, VP, VP, I32, I32, I32, VP]),
         "kie_debug_barrier": (ctypes.c_int, [I32, I32, I32, P(I32), P(ctypes.c_float), VP]),
+        "kie_debug_read_trace": (ctypes.c_int, [VP, P(ctypes.c_uint64), I32, P(I32), P(I32)]),
+        "kie_debug_stream": (ctypes.c_int, [VP, VP, ctypes.c_size_t, I32, I32, P(ctypes.c_float), VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -13,6 +13,12 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxGroup = 4;               // query heads per KV head
 constexpr int kMaxHeadDim = 128;           // 16 lanes x 8 fp16 per K/V row
 constexpr int kMaxActiveExperts = 16;      // top_k + shared
+constexpr int kBatch = 8;                  // GEMV: 16-byte loads per lane per batch
+constexpr int kPartCap = 2048;             // GEMV: per-block task partials in LDS (floats)
+constexpr int kGroups = 8;                 // grid barrier: arrival groups (one per XCD)
+constexpr int kGroupStride = 64;           // grid barrier: words between counters (256 B)
+constexpr int kBarrierWords = kGroupStride * (1 + kGroups);
+constexpr int kTraceEvents = 1024;         // trace slots per workgroup
 
 // Status codes written by the device into Params::err (same values as kie_status).
 constexpr int kErrTimeout = -7;
@@ -48,7 +54,7 @@ struct Params {
   float* u;                     // [max(F, (topk+nshared)*Fe)]  FFN hidden
   float* part;                  // [H][splits][hd+2]  split-K partial (acc, m, l)
   float* router_logits;         // [E]
-  unsigned* bar;                // grid barrier counter
+  unsigned* bar;                // grid barrier counters [kBarrierWords]
   unsigned* head_ctr;           // [nkv] split arrivals per KV head
   unsigned long long* amax;     // [2] packed (logit, index) argmax slots
   int* err;                     // device error word (0 = ok)
@@ -63,28 +69,41 @@ struct Params {
   float* out_logits;            // decode: [n_steps][Vout] or nullptr
   long long timeout_ticks;      // barrier watchdog in wall-clock ticks
   int spin_limit;               // > 0: cap on polls per wait (forced-watchdog tests)
+  unsigned long long* trace;    // [n_wg][kTraceEvents] barrier clock stamps, or nullptr
+  int trace_step;               // the decode step that is traced
 };
 
 // Host-visible launchers implemented next to the kernels.
-int max_blocks_per_cu(size_t lds_bytes);
-hipError_t launch_mono(const Params& p, size_t lds_bytes, hipStream_t s);
+int max_blocks_per_cu(int group, size_t lds_bytes);
+// p_dev: a device copy of p (the persistent kernel re-reads it per stage)
+hipError_t launch_mono(const Params& p, const Params* p_dev, size_t lds_bytes, bool plain,
+                       hipStream_t s);
 hipError_t launch_staged_step(const Params& p, size_t lds_bytes, hipStream_t s);
 hipError_t launch_gemv(const __half* w, const float* x, float* y, int rows, int cols, int n_wg,
                        hipStream_t s);
-hipError_t launch_barrier_test(unsigned* bar, int* slots, int* violations, int* err, int n_wg,
+size_t gemv_lds_bytes(int cols);
+hipError_t launch_barrier_test(unsigned* bar, unsigned* slots, int* violations, int* err, int n_wg,
                                int rounds, long long timeout_ticks, int spin_limit,
                                hipStream_t s);
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, unsigned* sink,
+                         hipStream_t s);
 
 // Dynamic LDS layout (in floats) shared by host and device:
-//   [0, hcap)            GEMV input vector (largest GEMV input length) or the
-//                        attention unit's q / new-KV / per-wave state area
-//   [red_off, total)     small reduction / routing area
+//   [0, hcap)               GEMV input vector (largest GEMV input length) or
+//                           the attention unit's q / new-KV / per-wave state
+//   [part_off, +kPartCap)   GEMV per-task partials of one row block
+//   [sums_off, +kPartCap)   GEMV row sums of one row block; MoE router logits
+//   [red_off, +kRedFloats)  reductions, argmax keys, MoE routing
 struct LdsLayout {
   int hcap;
+  int part_off;
+  int sums_off;
   int red_off;
   int total;
 };
-constexpr int kRedFloats = 2 * kWaves + 2 * kMaxActiveExperts + 64;
+constexpr int kRedIdsOff = 2 * kWaves;                       // int[kMaxActiveExperts]
+constexpr int kRedWtsOff = kRedIdsOff + kMaxActiveExperts;   // float[kMaxActiveExperts]
+constexpr int kRedFloats = kRedWtsOff + kMaxActiveExperts;
 
 __host__ __device__ inline LdsLayout lds_layout(const Params& p) {
   int v = p.d;
@@ -98,8 +117,10 @@ __host__ __device__ inline LdsLayout lds_layout(const Params& p) {
   v = v > attn ? v : attn;
   LdsLayout L;
   L.hcap = (v + 63) & ~63;
-  L.red_off = L.hcap;
-  L.total = L.hcap + kRedFloats;
+  L.part_off = L.hcap;
+  L.sums_off = L.part_off + kPartCap;
+  L.red_off = L.sums_off + kPartCap;
+  L.total = L.red_off + kRedFloats;
   return L;
 }
 

@@ -89,12 +89,15 @@ struct kie_handle {
   std::vector<void*> allocs;     // every hipMalloc of this handle
   kie::LayerPtrs* d_layers = nullptr;
   int* d_prompt = nullptr;
+  kie::Params* d_params = nullptr;   // device copy of the launch's parameter block
+  kie::Params call{};                // host source of that copy (outlives the async copy)
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
   int pos = 0;
   bool pending = false;
   bool broken = false;
   int last_decode_steps = 0;
+  int trace_events = 0;          // events per workgroup recorded by the last decode
 };
 
 namespace {
@@ -122,7 +125,7 @@ void free_handle(kie_handle* h) {
 // Clears barrier/argmax/error words before a launch (outside any capture).
 int reset_sync_words(kie_handle* h) {
   const kie::Params& b = h->base;
-  KIE_HIP(hipMemsetAsync(b.bar, 0, sizeof(unsigned), h->stream));
+  KIE_HIP(hipMemsetAsync(b.bar, 0, sizeof(unsigned) * kie::kBarrierWords, h->stream));
   KIE_HIP(hipMemsetAsync(b.head_ctr, 0, sizeof(unsigned) * b.nkv, h->stream));
   KIE_HIP(hipMemsetAsync(b.amax, 0, 2 * sizeof(unsigned long long), h->stream));
   KIE_HIP(hipMemsetAsync(b.err, 0, sizeof(int), h->stream));
@@ -151,8 +154,12 @@ int run_steps(kie_handle* h, kie::Params& p) {
   if (rc) return rc;
   const bool staged = (h->cfg.flags & KIE_MODE_GRAPH) != 0;
   if (!staged) {
+    h->call = p;
+    KIE_HIP(hipMemcpyAsync(h->d_params, &h->call, sizeof(kie::Params), hipMemcpyHostToDevice,
+                           h->stream));
     KIE_HIP(hipEventRecord(h->ev0, h->stream));
-    KIE_HIP(kie::launch_mono(p, h->lds, h->stream));
+    KIE_HIP(kie::launch_mono(p, h->d_params, h->lds, (h->cfg.flags & KIE_PLAIN_LAUNCH) != 0,
+                             h->stream));
     return finish_launch(h);
   }
   // Staged mode.  Decode: one step's kernels are captured into a hipGraph
@@ -229,7 +236,8 @@ int kie_config_check(const kie_config* c) {
   if (c->max_seq < 1 || c->max_seq > (1 << 20)) return fail(KIE_ERR_INVALID_ARG, "max_seq out of range");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(KIE_ERR_INVALID_ARG, "rms_eps must be >= 0");
   if (!(c->rope_base > 1.f) || !std::isfinite(c->rope_base)) return fail(KIE_ERR_INVALID_ARG, "rope_base must be > 1");
-  if (c->flags & ~KIE_MODE_GRAPH) return fail(KIE_ERR_INVALID_ARG, "unknown flag bits");
+  if (c->flags & ~(KIE_MODE_GRAPH | KIE_TRACE | KIE_PLAIN_LAUNCH))
+    return fail(KIE_ERR_INVALID_ARG, "unknown flag bits");
   if (c->n_workgroups < 0 || c->n_workgroups > 4096) return fail(KIE_ERR_INVALID_ARG, "n_workgroups out of range");
   if (c->timeout_ms < 0) return fail(KIE_ERR_INVALID_ARG, "timeout_ms < 0");
   kie::Params p = shape_params(*c);
@@ -295,7 +303,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   p.splits = std::max(1, p.n_wg / p.nkv);
   const kie::LdsLayout L = kie::lds_layout(p);
   h->lds = (size_t)L.total * sizeof(float);
-  const int per_cu = kie::max_blocks_per_cu(h->lds);
+  const int per_cu = kie::max_blocks_per_cu(c.n_heads / c.n_kv_heads, h->lds);
   if (per_cu < 1 || (long long)per_cu * n_cu < p.n_wg)
     return bail(fail(KIE_ERR_OCCUPANCY, "grid of " + std::to_string(p.n_wg) +
                                             " workgroups cannot be co-resident (" +
@@ -329,15 +337,20 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   KIE_ALLOC(u, float, ucount);
   KIE_ALLOC(part, float, (size_t)c.n_heads * p.splits * (hd + 2));
   KIE_ALLOC(router_logits, float, std::max(1, c.n_experts));
-  KIE_ALLOC(bar, unsigned, 1);
+  KIE_ALLOC(bar, unsigned, kie::kBarrierWords);
   KIE_ALLOC(head_ctr, unsigned, c.n_kv_heads);
   KIE_ALLOC(amax, unsigned long long, 2);
   KIE_ALLOC(err, int, 1);
   KIE_ALLOC(state, int, 4);
   KIE_ALLOC(expert_log, int, c.n_experts ? cap * c.n_layers * c.top_k : 1);
+  if (c.flags & KIE_TRACE) {
+    KIE_ALLOC(trace, unsigned long long, (size_t)p.n_wg * kie::kTraceEvents);
+  }
 #undef KIE_ALLOC
   if ((rc = dev_alloc(h, sizeof(int) * cap, &ptr))) return bail(rc);
   h->d_prompt = static_cast<int*>(ptr);
+  if ((rc = dev_alloc(h, sizeof(kie::Params), &ptr))) return bail(rc);
+  h->d_params = static_cast<kie::Params*>(ptr);
   if ((rc = dev_alloc(h, sizeof(kie::LayerPtrs) * c.n_layers, &ptr))) return bail(rc);
   h->d_layers = static_cast<kie::LayerPtrs*>(ptr);
   p.layers = h->d_layers;
@@ -387,6 +400,7 @@ int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
       return fail(KIE_ERR_TOKEN_RANGE, "prompt token " + std::to_string(i) + " out of range");
   KIE_HIP(hipMemcpyAsync(h->d_prompt, tokens, sizeof(int) * n, hipMemcpyHostToDevice, h->stream));
   kie::Params p = h->base;
+  p.trace = nullptr;
   p.mode = kie::kPrefill;
   p.n_steps = n - 1;
   p.pos0 = 0;
@@ -418,10 +432,17 @@ int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits)
   p.pos0 = h->pos;
   p.out_tokens = out_tokens;
   p.out_logits = out_logits;
+  p.trace_step = n > 1 ? 1 : 0;
   rc = run_steps(h, p);
   if (rc) return rc;
   h->pos += n;
   h->last_decode_steps = n;
+  if (p.trace) {
+    const int per_layer = h->cfg.n_experts ? 6 : 5;
+    // step start, then arrive/leave for every barrier: per_layer per layer and
+    // one after the lm_head stage
+    h->trace_events = std::min(kie::kTraceEvents, 1 + 2 * (h->cfg.n_layers * per_layer + 1));
+  }
   return KIE_OK;
 }
 
@@ -487,6 +508,25 @@ int kie_debug_expert_ids(const kie_handle* h, int32_t* ids_host, int32_t n_steps
   return KIE_OK;
 }
 
+int kie_debug_read_trace(const kie_handle* h, uint64_t* out, int32_t max_events, int32_t* n_events,
+                         int32_t* n_workgroups) {
+  g_err.clear();
+  if (!h || !out || !n_events) return fail(KIE_ERR_INVALID_ARG, "handle, out or n_events is NULL");
+  if (!h->base.trace || h->trace_events == 0)
+    return fail(KIE_ERR_BAD_STATE, "no trace: create with KIE_TRACE and call kie_decode first");
+  if (max_events < h->trace_events) return fail(KIE_ERR_INVALID_ARG, "max_events too small");
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  const int nwg = h->base.n_wg, ne = h->trace_events;
+  std::vector<unsigned long long> buf((size_t)nwg * kie::kTraceEvents);
+  KIE_HIP(hipMemcpy(buf.data(), h->base.trace, sizeof(unsigned long long) * buf.size(),
+                    hipMemcpyDeviceToHost));
+  for (int w = 0; w < nwg; ++w)
+    for (int e = 0; e < ne; ++e) out[(size_t)w * max_events + e] = buf[(size_t)w * kie::kTraceEvents + e];
+  *n_events = ne;
+  if (n_workgroups) *n_workgroups = nwg;
+  return KIE_OK;
+}
+
 int kie_debug_gemv(const void* w, const float* x, float* y, int32_t rows, int32_t cols,
                    int32_t n_wg, void* hip_stream) {
   g_err.clear();
@@ -520,14 +560,15 @@ int kie_debug_barrier(int32_t n_wg, int32_t rounds, int32_t spin_limit, int32_t*
   if (grid > n_cu) return fail(KIE_ERR_OCCUPANCY, "barrier test runs one workgroup per CU at most");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   void* mem = nullptr;
-  const size_t bytes = 64 + sizeof(int) * (size_t)grid;
+  const size_t bar_bytes = sizeof(unsigned) * kie::kBarrierWords;
+  const size_t bytes = bar_bytes + 256 + sizeof(unsigned) * (size_t)grid;
   KIE_HIP(hipMalloc(&mem, bytes));
   int rc = KIE_OK;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   unsigned* bar = static_cast<unsigned*>(mem);
-  int* viol = reinterpret_cast<int*>(static_cast<char*>(mem) + 16);
-  int* err = reinterpret_cast<int*>(static_cast<char*>(mem) + 32);
-  int* slots = reinterpret_cast<int*>(static_cast<char*>(mem) + 64);
+  int* viol = reinterpret_cast<int*>(static_cast<char*>(mem) + bar_bytes);
+  int* err = reinterpret_cast<int*>(static_cast<char*>(mem) + bar_bytes + 128);
+  unsigned* slots = reinterpret_cast<unsigned*>(static_cast<char*>(mem) + bar_bytes + 256);
   do {
     if (hipMemsetAsync(mem, 0, bytes, s) != hipSuccess || hipEventCreate(&e0) != hipSuccess ||
         hipEventCreate(&e1) != hipSuccess || hipEventRecord(e0, s) != hipSuccess) {
@@ -556,6 +597,45 @@ int kie_debug_barrier(int32_t n_wg, int32_t rounds, int32_t spin_limit, int32_t*
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   (void)hipFree(mem);
+  return rc;
+}
+
+int kie_debug_stream(const void* src, void* dst, size_t bytes, int32_t n_wg, int32_t reps,
+                     float* ms_per_launch, void* hip_stream) {
+  g_err.clear();
+  if (bytes == 0 || bytes % 16 != 0 || reps < 1 || reps > 10000 || n_wg < 0 || n_wg > 65536)
+    return fail(KIE_ERR_INVALID_ARG, "need bytes a positive multiple of 16, 1 <= reps <= 10000");
+  int rc;
+  if ((rc = check_device_range(src, bytes, "src"))) return rc;
+  if (dst && (rc = check_device_range(dst, bytes, "dst"))) return rc;
+  int dev = 0, n_cu = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  KIE_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  const int grid = n_wg > 0 ? n_wg : 4 * n_cu;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* sink = nullptr;
+  KIE_HIP(hipMalloc(&sink, 256));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  do {
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
+        hipEventRecord(e0, s) != hipSuccess) {
+      rc = fail(KIE_ERR_HIP, "stream probe setup failed");
+      break;
+    }
+    hipError_t e = hipSuccess;
+    for (int r = 0; r < reps && e == hipSuccess; ++r)
+      e = kie::launch_stream(src, dst, bytes, grid, static_cast<unsigned*>(sink), s);
+    float ms = 0.f;
+    if (e != hipSuccess || hipEventRecord(e1, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      rc = fail(KIE_ERR_HIP, "stream probe launch failed");
+      break;
+    }
+    if (ms_per_launch) *ms_per_launch = ms / (float)reps;
+  } while (0);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(sink);
   return rc;
 }
 

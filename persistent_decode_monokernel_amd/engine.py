@@ -18,7 +18,8 @@ _CFG_FIELDS = ("n_layers", "d_model", "n_heads", "n_kv_heads", "head_dim", "ffn_
 
 
 def make_config(model, max_seq: Optional[int] = None, graph: bool = False,
-                n_workgroups: int = 0, timeout_ms: int = 0) -> Config:
+                n_workgroups: int = 0, timeout_ms: int = 0, trace: bool = False,
+                plain_launch: bool = False) -> Config:
     """kie_config from any object with the model-shape attributes."""
     c = Config()
     for f in _CFG_FIELDS:
@@ -26,7 +27,8 @@ def make_config(model, max_seq: Optional[int] = None, graph: bool = False,
     if max_seq is None:
         max_seq = getattr(model, "kv_capacity")
     c.max_seq = int(max_seq)
-    c.flags = _lib.KIE_MODE_GRAPH if graph else 0
+    c.flags = ((_lib.KIE_MODE_GRAPH if graph else 0) | (_lib.KIE_TRACE if trace else 0)
+               | (_lib.KIE_PLAIN_LAUNCH if plain_launch else 0))
     c.n_workgroups = int(n_workgroups)
     c.timeout_ms = int(timeout_ms)
     return c
@@ -50,10 +52,11 @@ class Engine:
     """One decoder handle (kie_create .. kie_destroy)."""
 
     def __init__(self, model, weights: dict, max_seq: Optional[int] = None, graph: bool = False,
-                 n_workgroups: int = 0, timeout_ms: int = 0, stream: Optional[torch.cuda.Stream] = None):
+                 n_workgroups: int = 0, timeout_ms: int = 0, stream: Optional[torch.cuda.Stream] = None,
+                 trace: bool = False, plain_launch: bool = False):
         self.lib = _lib.load()
         self.model = model
-        self.cfg = make_config(model, max_seq, graph, n_workgroups, timeout_ms)
+        self.cfg = make_config(model, max_seq, graph, n_workgroups, timeout_ms, trace, plain_launch)
         self._weights = weights                       # keep the device memory alive
         L = model.n_layers
         self._layers = (LayerWeights * L)()
@@ -120,6 +123,18 @@ class Engine:
                                             n_steps), "kie_debug_expert_ids")
         return ids
 
+    def read_trace(self) -> np.ndarray:
+        """Barrier clock stamps of the traced step: uint64 [n_workgroups, n_events]
+        (event 0 = step start, then arrive/leave per grid barrier)."""
+        n_wg = 4096
+        buf = np.zeros((n_wg, 1024), np.uint64)
+        ne = ctypes.c_int32()
+        nw = ctypes.c_int32()
+        check(self.lib.kie_debug_read_trace(self.h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                            1024, ctypes.byref(ne), ctypes.byref(nw)),
+              "kie_debug_read_trace")
+        return buf[:nw.value, :ne.value].copy()
+
     def close(self) -> None:
         if getattr(self, "h", None) is not None and self.h.value:
             self.lib.kie_destroy(self.h)
@@ -160,4 +175,20 @@ def debug_barrier(n_workgroups: int = 0, rounds: int = 1000, spin_limit: int = 0
     return v.value, ms.value
 
 
-__all__ = ["Engine", "KieError", "make_config", "config_check", "debug_gemv", "debug_barrier"]
+def debug_stream(src: torch.Tensor, dst: Optional[torch.Tensor] = None, n_workgroups: int = 0,
+                 reps: int = 10) -> float:
+    """HBM streaming probe: ms per launch to read ``src`` (and copy it to ``dst``)."""
+    lib = _lib.load()
+    ms = ctypes.c_float()
+    s = torch.cuda.current_stream()
+    nbytes = src.numel() * src.element_size()
+    if dst is not None and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst must have the size of src")
+    check(lib.kie_debug_stream(src.data_ptr(), dst.data_ptr() if dst is not None else None,
+                               nbytes, n_workgroups, reps, ctypes.byref(ms),
+                               ctypes.c_void_p(s.cuda_stream)), "kie_debug_stream")
+    return ms.value
+
+
+__all__ = ["Engine", "KieError", "make_config", "config_check", "debug_gemv", "debug_barrier",
+           "debug_stream"]

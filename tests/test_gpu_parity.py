@@ -10,7 +10,7 @@ import pytest
 
 from kie_synth import get_config, make_prompt, make_weights, weights_to_numpy
 from oracle import Oracle
-from tests.parity import compare_steps, kv_close
+from tests.parity import compare_steps, kv_close, kv_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +95,20 @@ def _oracle_replay(cfg, Wn, prompt, toks):
     return o, z
 
 
-@pytest.mark.parametrize("mode", ["persistent", "graph", "persistent_7wg", "graph_5wg"])
+def _check_kv(eng, o, layers, spans):
+    """Layer 0 sees identical inputs on both sides: half an fp16 ulp.  Every
+    listed layer: each row within 1e-2 of its largest magnitude."""
+    for l in layers:
+        for p0, p1 in spans:
+            k, v = eng.read_kv(l, p0, p1)
+            if l == 0:
+                kv_close(k, o.K[0][:, p0:p1], f"K layer 0 [{p0},{p1})")
+                kv_close(v, o.V[0][:, p0:p1], f"V layer 0 [{p0},{p1})")
+            kv_rows_close(k, o.K[l][:, p0:p1], f"K layer {l} [{p0},{p1})")
+            kv_rows_close(v, o.V[l][:, p0:p1], f"V layer {l} [{p0},{p1})")
+
+
+@pytest.mark.parametrize("mode", ["persistent", "graph", "persistent_7wg", "graph_5wg", "persistent_3wg"])
 def test_tiny_decode_parity(torch, kie, mode):
     cfg = _model("tiny")
     _say("tiny parity", mode)
@@ -113,10 +126,7 @@ def test_tiny_decode_parity(torch, kie, mode):
     assert rep["pinned"] >= cfg.n_decode // 2
     # KV cache rows (after RoPE for K) at every written position
     P = len(prompt)
-    for l in range(cfg.n_layers):
-        k, v = eng.read_kv(l, 0, P - 1 + cfg.n_decode)
-        kv_close(k, o.K[l][:, :P - 1 + cfg.n_decode], f"K layer {l}")
-        kv_close(v, o.V[l][:, :P - 1 + cfg.n_decode], f"V layer {l}")
+    _check_kv(eng, o, range(cfg.n_layers), [(0, P - 1 + cfg.n_decode)])
     eng.close()
 
 
@@ -209,9 +219,6 @@ def test_2b_full_size_parity_sampled(torch, kie):
     rep = compare_steps(z, toks, zo)
     _say("2b", rep)
     P = len(prompt)
-    for l in (0, 12, 24):
-        for p0 in (0, 255, P - 2, P - 1 + n - 1):
-            k, v = eng.read_kv(l, p0, p0 + 1)
-            kv_close(k, o.K[l][:, p0:p0 + 1], f"K l{l} p{p0}")
-            kv_close(v, o.V[l][:, p0:p0 + 1], f"V l{l} p{p0}")
+    _check_kv(eng, o, (0, 12, 24),
+              [(0, 1), (255, 256), (P - 2, P - 1), (P - 1 + n - 1, P - 1 + n)])
     eng.close()
