@@ -84,36 +84,37 @@ def cpu_baseline(cfg, W, prompt, budget_s: float):
 
 
 def trace_summary(cfg, tr):
-    """Per-stage timing of one traced decode step from the in-kernel barrier
-    stamps (100 MHz wall clock): for each stage kind, the mean over layers of
-    the mean and the max over workgroups of the time from leaving the
-    previous barrier to arriving at the next, and of the time spent waiting
-    in the barrier."""
+    """Per-stage timing of one traced decode step from the in-kernel clock
+    stamps (100 MHz wall clock).  Each stage records when its inputs were
+    complete ("ready") and when it finished ("end"); "wait" is ready minus
+    the workgroup's previous end, "work" is end minus ready.  Reported per
+    stage kind: the mean over layers of the mean and max over workgroups."""
     import numpy as np
     t = tr.astype(np.float64) * 10.0 / 1000.0          # ticks of 10 ns -> us
     t -= t[:, :1]
-    kinds = (["qkv", "attn", "o", "router", "gateup", "down"] if cfg.n_experts
+    kinds = (["qkv", "attn", "o", "router", "moe_gateup", "moe_down"] if cfg.n_experts
              else ["qkv", "attn", "o", "gateup", "down"])
-    names = [f"{k}" for _ in range(cfg.n_layers) for k in kinds] + ["lm_head"]
-    nb = (t.shape[1] - 1) // 2
+    names = [k for _ in range(cfg.n_layers) for k in kinds] + ["lm_head"]
     out = {}
-    prev_leave = t[:, 0]
-    for k in range(min(nb, len(names))):
-        arrive, leave = t[:, 1 + 2 * k], t[:, 2 + 2 * k]
-        work = arrive - prev_leave
-        wait = leave - arrive
-        d = out.setdefault(names[k], {"n": 0, "work_mean_us": 0.0, "work_max_us": 0.0,
-                                      "wait_mean_us": 0.0, "span_us": 0.0})
+    prev_end = t[:, 0]
+    for k, name in enumerate(names):
+        if 2 + 2 * k >= t.shape[1]:
+            break
+        ready, end = t[:, 1 + 2 * k], t[:, 2 + 2 * k]
+        wait, work = ready - prev_end, end - ready
+        d = out.setdefault(name, {"n": 0, "wait_mean_us": 0.0, "wait_max_us": 0.0,
+                                  "work_mean_us": 0.0, "work_max_us": 0.0})
         d["n"] += 1
+        d["wait_mean_us"] += float(wait.mean())
+        d["wait_max_us"] += float(wait.max())
         d["work_mean_us"] += float(work.mean())
         d["work_max_us"] += float(work.max())
-        d["wait_mean_us"] += float(wait.mean())
-        d["span_us"] += float(leave.max() - prev_leave.min())
-        prev_leave = leave
+        prev_end = end
     for d in out.values():
-        for key in ("work_mean_us", "work_max_us", "wait_mean_us", "span_us"):
+        for key in ("wait_mean_us", "wait_max_us", "work_mean_us", "work_max_us"):
             d[key] /= d["n"]
-    return {"step_us": float(t[:, -1].max()), "stages": out}
+    barrier = float((t[:, -1] - prev_end).mean())
+    return {"step_us": float(t[:, -1].max()), "argmax_barrier_mean_us": barrier, "stages": out}
 
 
 def hbm_probes(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 10) -> dict:

@@ -255,7 +255,6 @@ __device__ __forceinline__ GridSync make_sync(unsigned* ctr, int* err, unsigned 
 }
 
 __device__ __forceinline__ void grid_arrive(GridSync& g) {
-  trace_mark(g);
   wait_stores();
   __builtin_amdgcn_s_barrier();
   g.epoch += 1u;
@@ -304,7 +303,6 @@ __device__ __forceinline__ bool grid_wait(GridSync& g, int* flag) {
   }
   __syncthreads();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  trace_mark(g);
   return *flag != 0;
 }
 
@@ -344,7 +342,9 @@ __device__ __forceinline__ GemvWork gemv_work(int rows, int cols, int parts, int
 struct WBatch {
   u32x4 w[kBatch];
 };
-typedef WBatch WPre;           // the first batch of a wave's first block
+struct WPre {                  // the first two batches of a wave's first block
+  WBatch a, b;
+};
 
 __device__ __forceinline__ void wave_tasks(const GemvWork& g, int b0, int& t0, int& t1) {
   const int b1 = min(g.r1, b0 + g.rb);
@@ -402,18 +402,21 @@ template <class Addr>
 __device__ __forceinline__ WPre gemv_prefetch(const GemvWork& g, const Addr& addr) {
   int t0, t1;
   wave_tasks(g, g.r0, t0, t1);
-  return wload(addr, g, g.r0, t0, t1);
+  WPre P;
+  P.a = wload(addr, g, g.r0, t0, t1);
+  P.b = wload(addr, g, g.r0, t0 + kBatch, t1);
+  return P;
 }
 
-// One row block [b0, b0 + nrows): A holds the wave's first batch (already
-// issued); the rest of the block streams through A and B.
+// One row block [b0, b0 + nrows): A and B hold the wave's first two
+// batches (already issued); the rest of the block streams through them.
 template <class Addr, class Epi>
 __device__ __forceinline__ void gemv_block(const GemvWork& g, const Addr& addr, const float* h,
-                                           float* part, float* sums, int b0, WBatch A, Epi& epi) {
+                                           float* part, float* sums, int b0, WBatch A, WBatch B,
+                                           Epi& epi) {
   const int nrows = min(g.r1 - b0, g.rb);
   int t0, t1;
   wave_tasks(g, b0, t0, t1);
-  WBatch B = wload(addr, g, b0, t0 + kBatch, t1);
   for (int t = t0; t < t1; t += 2 * kBatch) {
     wconsume(A, h, g, t, t1, part);
     if (t + 2 * kBatch < t1) A = wload(addr, g, b0, t + 2 * kBatch, t1);
@@ -441,24 +444,180 @@ __device__ __forceinline__ void gemv_run(const GemvWork& g, const Addr& addr, co
   if (g.r0 >= g.r1) return;
   int b0 = g.r0;
   if (kPre) {
-    gemv_block(g, addr, h, part, sums, b0, pre, epi);
+    gemv_block(g, addr, h, part, sums, b0, pre.a, pre.b, epi);
     b0 += g.rb;
   }
   for (; b0 < g.r1; b0 += g.rb) {
     int t0, t1;
     wave_tasks(g, b0, t0, t1);
-    gemv_block(g, addr, h, part, sums, b0, wload(addr, g, b0, t0, t1), epi);
+    const WBatch A = wload(addr, g, b0, t0, t1);
+    const WBatch B = wload(addr, g, b0, t0 + kBatch, t1);
+    gemv_block(g, addr, h, part, sums, b0, A, B, epi);
   }
 }
 
 // ---------------------------------------------------------------------------
+// Activation exchange: flag-in-data words.
+//
+// Every activation one workgroup hands to others (x, q/k/v, attention
+// partials, o, the FFN hidden u, router logits) lives in one arena of 64-bit
+// words: the low half is the fp32 value, the high half the epoch of the
+// stage that wrote it.  A producer writes each word with one device-scope
+// 64-bit store (single-copy atomic), so a consumer that reads a word with
+// the epoch it expects also has the value: one load both synchronises and
+// delivers, and stages need no grid barrier and no store-completion wait.
+// Epochs are unique per (call, step, layer, stage slot): flag(step, l, slot)
+// = epoch0 + (step * L + l) * 8 + slot, with epoch0 advanced by the host
+// for every launch, so stale words of earlier stages or calls never match.
+//
+// Reuse of a word by a later stage is safe without barriers because every
+// stage that writes a buffer depends (through the data it consumes) on
+// every workgroup having finished the stage that read the previous value:
+// e.g. x written by the O projection of layer l+1 needs o of every head,
+// hence every Q/K/V row of layer l+1, hence every workgroup's read of x in
+// that layer's Q/K/V stage.  Consecutive decode steps are separated by the
+// argmax grid barrier, consecutive prefill steps by an explicit barrier.
+// ---------------------------------------------------------------------------
+typedef unsigned long long u64;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum Slot : unsigned { kSlotQkv = 0, kSlotPart = 1, kSlotO = 2, kSlotXO = 3, kSlotRouter = 4,
+                       kSlotU = 5, kSlotXDown = 6 };
+
+__device__ __forceinline__ unsigned ll_flag(const Params& p, int step, int l, unsigned slot) {
+  return p.epoch0 + ((unsigned)step * (unsigned)p.L + (unsigned)l) * 8u + slot;
+}
+
+__device__ __forceinline__ void ll_put(const Params& p, int word, float v, unsigned flag) {
+  const u64 w = ((u64)flag << 32) | (u64)__float_as_uint(v);
+  __hip_atomic_store(p.act + word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ Rsrc arena_rsrc(const Params& p) {
+  return make_rsrc(p.act, (size_t)p.act_words * 8);
+}
+
+__device__ __forceinline__ u32x2 ld_ll(Rsrc r, unsigned byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kAuxSc1));
+}
+
+// A contiguous run of arena words to copy into LDS once they carry `want`.
+typedef __attribute__((address_space(3))) float lds_float;
+struct LLRange {
+  int src;            // first arena word
+  int n;              // words
+  float* dst;         // LDS destination
+  unsigned want;      // expected epoch
+};
+
+// Control state shared by every bounded wait of a workgroup.
+struct Ctl {
+  int* err;
+  long long ticks;
+  int spin_limit;
+  int* flag;          // LDS int used to make results workgroup-uniform
+};
+
+__device__ __forceinline__ Ctl make_ctl(const Params& p, int* flag) {
+  return Ctl{p.err, p.timeout_ticks, p.spin_limit, flag};
+}
+
+// Workgroup-uniform AND of `ok` (every thread passes its own value).
+__device__ __forceinline__ bool wg_all(bool ok, int* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = 1;
+  __syncthreads();
+  if (!ok) *flag = 0;
+  __syncthreads();
+  return *flag != 0;
+}
+
+constexpr int kGatherPer = 8;    // words per thread per pass
+
+// Copies up to NR ranges of the arena into LDS, waiting until every word
+// carries its range's epoch.  Thread t owns words t, t + kThreads, ... of
+// the concatenated ranges and re-reads only the ones not yet valid; loads
+// are issued for all of them at once.  Returns false (uniformly) when a
+// wait passes the timeout or another workgroup reported an error.
+template <int NR>
+__device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c) {
+  const Rsrc arena = arena_rsrc(p);
+  int total = 0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) total += rg[r].n;
+  bool ok = true;
+  for (int seg = 0; seg < total && ok; seg += kGatherPer * kThreads) {
+    unsigned pending = 0;
+    unsigned off[kGatherPer];
+    unsigned want[kGatherPer];
+    lds_float* dst[kGatherPer];       // 32-bit LDS addresses
+#pragma unroll
+    for (int k = 0; k < kGatherPer; ++k) {
+      int i = seg + (int)threadIdx.x + k * kThreads;
+      off[k] = kOffNone;
+      want[k] = 0u;
+      dst[k] = nullptr;
+      if (i < total) {
+        pending |= 1u << k;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if (i >= 0 && i < rg[r].n) {
+            off[k] = (unsigned)(rg[r].src + i) * 8u;
+            want[k] = rg[r].want;
+            dst[k] = (lds_float*)(rg[r].dst + i);
+          }
+          i -= rg[r].n;
+        }
+      }
+    }
+    long long t0 = 0;
+    int spins = 0;
+    while (pending) {
+      u32x2 v[kGatherPer];
+#pragma unroll
+      for (int k = 0; k < kGatherPer; ++k) v[k] = ld_ll(arena, ((pending >> k) & 1u) ? off[k] : kOffNone);
+#pragma unroll
+      for (int k = 0; k < kGatherPer; ++k) {
+        if (((pending >> k) & 1u) && v[k].y == want[k]) {
+          *dst[k] = __uint_as_float(v[k].x);
+          pending &= ~(1u << k);
+        }
+      }
+      if (pending) {
+        ++spins;
+        if ((spins & 15) == 1) {
+          if (spins == 1) t0 = wall_clock64();
+          if (__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            ok = false;
+            break;
+          }
+          if (wall_clock64() - t0 > c.ticks) {
+            set_timeout(c.err);
+            ok = false;
+            break;
+          }
+        }
+        if (c.spin_limit > 0 && spins >= c.spin_limit) {
+          set_timeout(c.err);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  return wg_all(ok, c.flag);
+}
+
+// ---------------------------------------------------------------------------
 // LDS carve-up (floats): [0, hcap) GEMV vector / attention area; part;
-// sums; a small reduction / routing area.
+// sums; xown (this workgroup's rows of x); a small reduction / routing area.
 // ---------------------------------------------------------------------------
 struct Lds {
   float* h;
   float* part;
   float* sums;
+  float* xown;
   float* red;
 };
 
@@ -468,43 +627,85 @@ __device__ __forceinline__ Lds lds_carve(const Params& p, float* smem) {
   s.h = smem;
   s.part = smem + L.part_off;
   s.sums = smem + L.sums_off;
+  s.xown = smem + L.xown_off;
   s.red = smem + L.red_off;
   return s;
 }
 
-// RMSNorm into LDS, recomputed by every workgroup (deterministic, no extra
-// barrier): h = v / sqrt(mean(v^2) + eps) * gain with v = x (fp32, shared)
-// or, at layer 0, the fp16 embedding row.
-__device__ __forceinline__ void rmsnorm_to_lds(const Params& p, const float* xg, const __half* xe,
-                                               const __half* gain, float* h, float* red) {
+// Norm gains are read-only: their loads are issued before the wait for the
+// activations, for up to kGainPer * kThreads elements.
+constexpr int kGainPer = 8;
+struct GainPre {
+  float g[kGainPer];
+};
+__device__ __forceinline__ GainPre gain_prefetch(const __half* gain, int d) {
+  GainPre G;
+#pragma unroll
+  for (int k = 0; k < kGainPer; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    G.g[k] = i < d ? __half2float(gain[i]) : 0.f;
+  }
+  return G;
+}
+
+// RMSNorm of the d values in h (LDS), in place, recomputed by every
+// workgroup in a fixed order: h = v / sqrt(mean(v^2) + eps) * gain.
+__device__ __forceinline__ void rmsnorm_lds(const Params& p, const __half* gain, const GainPre& G,
+                                            float* h, float* red) {
   const int d = p.d;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += kThreads) {
-    const float v = xg ? ld_c(xg + i) : __half2float(xe[i]);
-    h[i] = v;
-    ss = fmaf(v, v, ss);
-  }
+  for (int i = threadIdx.x; i < d; i += kThreads) ss = fmaf(h[i], h[i], ss);
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + p.eps);
-  for (int i = threadIdx.x; i < d; i += kThreads) h[i] = h[i] * inv * __half2float(gain[i]);
+#pragma unroll
+  for (int k = 0; k < kGainPer; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < d) h[i] = h[i] * inv * G.g[k];
+  }
+  for (int i = threadIdx.x + kGainPer * kThreads; i < d; i += kThreads)
+    h[i] = h[i] * inv * __half2float(gain[i]);
   __syncthreads();
 }
 
-__device__ __forceinline__ void copy_to_lds(const float* src, int n, float* h) {
-  for (int i = threadIdx.x; i < n; i += kThreads) h[i] = ld_c(src + i);
-  __syncthreads();
+// Appends one clock stamp to the workgroup's trace (traced steps only).
+struct Tracer {
+  unsigned long long* tr;
+  int ev;
+};
+__device__ __forceinline__ void mark(Tracer& t) {
+  if (t.tr != nullptr) {
+    if (threadIdx.x == 0 && t.ev < kTraceEvents) t.tr[t.ev] = wall_clock64();
+    ++t.ev;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Row address functors of each GEMV.
 // ---------------------------------------------------------------------------
+// A wave-uniform address as an opaque uniform value (readfirstlane of both
+// halves): keeps it in SGPRs and keeps the optimiser from folding a choice
+// between struct members into an indexed load of the struct.
+__device__ __forceinline__ uintptr_t uniform_addr(const void* p) {
+  const unsigned long long v = (unsigned long long)(uintptr_t)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (uintptr_t)(((unsigned long long)hi << 32) | lo);
+}
+
 // Each GEMV's weights as buffer resources: rsrc(r) is the resource holding
 // row r (uniform across the wave), off(r, c) the byte offset of 16-byte
 // chunk c of that row.  Every resource spans its whole tensor (< 4 GiB).
 struct QkvAddr {             // rows of Wq, then Wk, then Wv
-  Rsrc q, k, v;
+  const __half *wq, *wk, *wv;
   int qd, kd, d;
-  __device__ Rsrc rsrc(int r) const { return r < qd ? q : (r < qd + kd ? k : v); }
+  // The resource is built from a base pointer selected among opaque copies
+  // of the members: a select of the members themselves is folded into an
+  // indexed load from the functor, which then lives in scratch memory.
+  __device__ Rsrc rsrc(int r) const {
+    const bool isq = r < qd, isk = !isq && r < qd + kd;
+    const uintptr_t b = isq ? uniform_addr(wq) : (isk ? uniform_addr(wk) : uniform_addr(wv));
+    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)(isq ? qd : kd) * d * 2);
+  }
   __device__ unsigned off(int r, int c) const {
     const int rr = r < qd ? r : (r < qd + kd ? r - qd : r - qd - kd);
     return (unsigned)rr * (unsigned)d * 2u + (unsigned)c * 16u;
@@ -519,18 +720,24 @@ struct RowAddr {             // plain row-major [rows][cols]
   }
 };
 struct PairAddr {            // virtual row 2f = gate row f, 2f+1 = up row f
-  Rsrc gate, up;
-  int cols;
-  __device__ Rsrc rsrc(int vr) const { return (vr & 1) ? up : gate; }
+  const __half *gate, *up;
+  int rows, cols;
+  __device__ Rsrc rsrc(int vr) const {
+    const uintptr_t b = (vr & 1) ? uniform_addr(up) : uniform_addr(gate);
+    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)rows * cols * 2);
+  }
   __device__ unsigned off(int vr, int c) const {
     return (unsigned)(vr >> 1) * (unsigned)cols * 2u + (unsigned)c * 16u;
   }
 };
 struct MoePairAddr {         // virtual row 2f (+1): pair f = (slot f / Fe, row f % Fe)
-  Rsrc gate, up;             // whole stacked expert tensors
+  const __half *gate, *up;   // whole stacked expert tensors [E + S][Fe][d]
   const int* ids;            // LDS: expert id per active slot
-  int Fe, d;
-  __device__ Rsrc rsrc(int vr) const { return (vr & 1) ? up : gate; }
+  int ne, Fe, d;
+  __device__ Rsrc rsrc(int vr) const {
+    const uintptr_t b = (vr & 1) ? uniform_addr(up) : uniform_addr(gate);
+    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)ne * Fe * d * 2);
+  }
   __device__ unsigned off(int vr, int c) const {
     const int f = vr >> 1;
     const int a = f / Fe, ff = f - a * Fe;
@@ -554,6 +761,8 @@ __device__ __forceinline__ Rsrc mat_rsrc(const __half* w, int rows, int cols) {
 
 // ---------------------------------------------------------------------------
 // Stage: RMSNorm + fused Q/K/V GEMV (rows of Wq, Wk, Wv as one row space).
+// Layer 0 normalises the embedding row; later layers wait for x of the
+// previous layer's down projection.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ GemvWork qkv_work(const Params& p, int wg) {
   return gemv_work(p.H * p.hd + 2 * p.nkv * p.hd, p.d, p.n_wg, wg, false);
@@ -561,20 +770,35 @@ __device__ __forceinline__ GemvWork qkv_work(const Params& p, int wg) {
 __device__ __forceinline__ QkvAddr qkv_addr(const Params& p, int l) {
   const LayerPtrs& w = p.layers[l];
   const int qd = p.H * p.hd, kd = p.nkv * p.hd;
-  return QkvAddr{mat_rsrc(w.wq, qd, p.d), mat_rsrc(w.wk, kd, p.d), mat_rsrc(w.wv, kd, p.d), qd, kd, p.d};
+  return QkvAddr{w.wq, w.wk, w.wv, qd, kd, p.d};
 }
 __device__ __forceinline__ WPre prefetch_qkv(const Params& p, int l, int wg) {
   return gemv_prefetch(qkv_work(p, wg), qkv_addr(p, l));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_qkv(const Params& p, int l, const __half* emb_row, int wg, Lds s,
-                                          WPre pre) {
-  rmsnorm_to_lds(p, l == 0 ? nullptr : p.x, emb_row, p.layers[l].attn_norm, s.h, s.red);
-  float* out = p.qkv;
-  gemv_run<kPre>(qkv_work(p, wg), qkv_addr(p, l), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) st_c(out + b0 + i, sums[i]);
-           });
+__device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, const __half* emb_row,
+                                          int wg, Lds s, WPre pre, const Ctl& c, Tracer& tr) {
+  const GemvWork g = qkv_work(p, wg);
+  if (g.r0 >= g.r1) {
+    mark(tr);
+    return true;
+  }
+  const __half* gain = p.layers[l].attn_norm;
+  const GainPre G = gain_prefetch(gain, p.d);
+  if (l == 0) {
+    for (int i = threadIdx.x; i < p.d; i += kThreads) s.h[i] = __half2float(emb_row[i]);
+  } else {
+    const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l - 1, kSlotXDown)}};
+    if (!ll_gather(p, rg, c)) return false;
+  }
+  mark(tr);
+  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const unsigned f = ll_flag(p, step, l, kSlotQkv);
+  gemv_run<kPre>(g, qkv_addr(p, l), s.h, s.part, s.sums, pre,
+                 [&](int b0, int n, const float* sums) {
+                   for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_qkv + b0 + i, sums[i], f);
+                 });
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -587,9 +811,10 @@ __device__ __forceinline__ void stage_qkv(const Params& p, int l, const __half* 
 // 16-lane group; states are merged across groups, then waves, in a fixed
 // order.  The split containing the current position rotates the new key,
 // rounds K and V to fp16, appends them to the cache and uses the rounded
-// values.  Each split writes (acc, m, l) to HBM; the last split to arrive
-// at the per-head counter merges all splits in split order into o.
-// Scores carry log2(e)/sqrt(hd) so exp2 is the softmax exponential.
+// values.  With one split per head the unit writes o directly; otherwise
+// each split publishes its (acc, m, l) partial and split 0 of each head
+// merges all splits in split order into o.  Scores carry log2(e)/sqrt(hd)
+// so exp2 is the softmax exponential.
 // ---------------------------------------------------------------------------
 constexpr int kAttnStride = kWaves * 4;     // positions per workgroup per step
 constexpr int kAU = 4;                      // steps in flight
@@ -646,25 +871,76 @@ __device__ __forceinline__ KVPre prefetch_attn(const Params& p, int l, int pos, 
   return P;
 }
 
-template <int G, bool kPre>
-__device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const AttnUnit& U,
-                                          float* lds, int* flag, KVPre pre) {
+// LDS areas of an attention unit (floats, all inside [0, hcap)).
+struct AttnLds {
+  float *qs, *kn, *vn, *wst, *parts;
+};
+template <int G>
+__device__ __forceinline__ AttnLds attn_lds(const Params& p, float* lds) {
+  const int hd = p.hd;
+  AttnLds a;
+  a.qs = lds;                                  // [G][hd]
+  a.kn = a.qs + G * hd;                        // [hd]
+  a.vn = a.kn + hd;                            // [hd]
+  a.wst = a.vn + hd;                           // [kWaves][G][hd + 2]
+  a.parts = a.wst + kWaves * G * (hd + 2);     // [S][G][hd + 2] (merging split only)
+  return a;
+}
+
+// Arena word of split s's partial for query head (g*G + h), element i.
+__device__ __forceinline__ int part_word(const Params& p, int g, int G, int s, int h, int i) {
+  return p.off_part + (((g * p.splits + s) * G + h) * (p.hd + 2)) + i;
+}
+
+// Merges the S partials of head group g (in LDS, [S][G][hd+2]) in split
+// order and publishes o.
+template <int G>
+__device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, const float* parts) {
+  const int hd = p.hd, S = p.splits, ws = hd + 2;
+  const unsigned fo = ll_flag(p, step, l, kSlotO);
+  for (int t = threadIdx.x; t < G * hd; t += kThreads) {
+    const int h = t / hd, i = t % hd;
+    float M = kNegBig;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, parts[(s * G + h) * ws + hd]);
+    float Ls = 0.f, A = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float* st = parts + (s * G + h) * ws;
+      const float sc = exp2f(st[hd] - M);
+      Ls = fmaf(st[hd + 1], sc, Ls);
+      A = fmaf(st[i], sc, A);
+    }
+    ll_put(p, p.off_o + (g * G + h) * hd + i, A / Ls, fo);
+  }
+}
+
+// Gathers head group g's partials and merges them (split 0's workgroup in
+// the persistent kernel, or the merge kernel of the staged mode).
+template <int G>
+__device__ __forceinline__ bool attn_gather_merge(const Params& p, int step, int l, int g, float* lds,
+                                                  const Ctl& c) {
+  const AttnLds a = attn_lds<G>(p, lds);
+  const LLRange rg[1] = {{part_word(p, g, G, 0, 0, 0), p.splits * G * (p.hd + 2), a.parts,
+                          ll_flag(p, step, l, kSlotPart)}};
+  if (!ll_gather(p, rg, c)) return false;
+  attn_merge<G>(p, step, l, g, a.parts);
+  return true;
+}
+
+template <int G, bool kPre, bool kMerge>
+__device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int pos, const AttnUnit& U,
+                                          float* lds, KVPre pre, const Ctl& c, Tracer& tr) {
   const int hd = p.hd, half = hd >> 1, S = p.splits;
   const int qd = p.H * hd, kd = p.nkv * hd;
   const int g = U.g, sidx = U.sidx, p0 = U.p0, pend = U.pend;
   const bool has_new = U.has_new;
-
-  float* qs = lds;                               // [G][hd]
-  float* kn = qs + G * hd;                       // [hd]
-  float* vn = kn + hd;                           // [hd]
-  float* wst = vn + hd;                          // [kWaves][G][hd + 2]
+  const AttnLds a = attn_lds<G>(p, lds);
 
   const size_t hb = kv_head_base(p, l, g);
   const unsigned bytes = (unsigned)((size_t)p.cap * hd * 2);
   const Rsrc rk = make_rsrc(p.kc + hb, bytes);
   const Rsrc rv = make_rsrc(p.vc + hb, bytes);
 
-  // first step of cache rows: prefetched before the barrier, or now
+  // first step of cache rows: prefetched before the wait, or now
   u32x4 kr[kAU], vr[kAU];
   if (kPre) {
 #pragma unroll
@@ -676,44 +952,64 @@ __device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const
     kv_load_step(p, rk, rv, p0, pend, kr, vr);
   }
 
-  const float* qkv = p.qkv;
+  // raw q of the G heads (and the new k, v for the split holding pos)
+  {
+    const unsigned fq = ll_flag(p, step, l, kSlotQkv);
+    const LLRange rg[3] = {{p.off_qkv + g * G * hd, G * hd, a.qs, fq},
+                           {p.off_qkv + qd + g * hd, has_new ? hd : 0, a.kn, fq},
+                           {p.off_qkv + qd + kd + g * hd, has_new ? hd : 0, a.vn, fq}};
+    if (!ll_gather(p, rg, c)) return false;
+  }
+  mark(tr);
+
   const float* cs = p.rope_cos + (size_t)pos * half;
   const float* sn = p.rope_sin + (size_t)pos * half;
   const float qscale = kLog2e / sqrtf((float)hd);
-
-  for (int i = threadIdx.x; i < G * hd; i += kThreads) {
-    const int hq = g * G + i / hd, j = i % hd;
-    const float* q = qkv + (size_t)hq * hd;
-    const int jj = j < half ? j : j - half;
-    const float c = cs[jj], sv = sn[jj];
-    const float rot = j < half ? ld_c(q + j) * c - ld_c(q + j + half) * sv
-                               : ld_c(q + j) * c + ld_c(q + j - half) * sv;
-    qs[i] = rot * qscale;
-  }
-  if (has_new) {
-    const float* k = qkv + qd + (size_t)g * hd;
-    const float* v = qkv + qd + kd + (size_t)g * hd;
-    unsigned* kc32 = reinterpret_cast<unsigned*>(p.kc + hb + (size_t)pos * hd);
-    unsigned* vc32 = reinterpret_cast<unsigned*>(p.vc + hb + (size_t)pos * hd);
-    for (int jp = threadIdx.x; jp < half; jp += kThreads) {
-      // elements 2jp and 2jp+1 (one 32-bit store each for K and V)
-      __half kh[2], vh[2];
+  // rotate-half RoPE; every thread computes its elements from the raw values
+  // before any is overwritten
+  float qrot[(kMaxGroup * kMaxHeadDim + kThreads - 1) / kThreads];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int j = 2 * jp + e;
-        const int jj = j < half ? j : j - half;
-        const float c = cs[jj], sv = sn[jj];
-        const float rot = j < half ? ld_c(k + j) * c - ld_c(k + j + half) * sv
-                                   : ld_c(k + j) * c + ld_c(k + j - half) * sv;
-        kh[e] = __float2half_rn(rot);
-        vh[e] = __float2half_rn(ld_c(v + j));
-        kn[j] = __half2float(kh[e]);
-        vn[j] = __half2float(vh[e]);
-      }
-      const unsigned kw = (unsigned)__half_as_ushort(kh[0]) | ((unsigned)__half_as_ushort(kh[1]) << 16);
-      const unsigned vw = (unsigned)__half_as_ushort(vh[0]) | ((unsigned)__half_as_ushort(vh[1]) << 16);
-      st_cu(kc32 + jp, kw);
-      st_cu(vc32 + jp, vw);
+  for (int k = 0; k < (kMaxGroup * kMaxHeadDim + kThreads - 1) / kThreads; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    qrot[k] = 0.f;
+    if (i < G * hd) {
+      const int h = i / hd, j = i % hd;
+      const float* q = a.qs + h * hd;
+      const int jj = j < half ? j : j - half;
+      const float cc = cs[jj], sv = sn[jj];
+      qrot[k] = (j < half ? q[j] * cc - q[j + half] * sv : q[j] * cc + q[j - half] * sv) * qscale;
+    }
+  }
+  float krot = 0.f, vval = 0.f;
+  if (has_new && threadIdx.x < hd) {
+    const int j = threadIdx.x;
+    const int jj = j < half ? j : j - half;
+    const float cc = cs[jj], sv = sn[jj];
+    krot = j < half ? a.kn[j] * cc - a.kn[j + half] * sv : a.kn[j] * cc + a.kn[j - half] * sv;
+    vval = a.vn[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < (kMaxGroup * kMaxHeadDim + kThreads - 1) / kThreads; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < G * hd) a.qs[i] = qrot[k];
+  }
+  if (has_new && threadIdx.x < hd) {
+    // round to fp16 (RNE), use the rounded values, append them to the cache
+    const int j = threadIdx.x;
+    const __half kh = __float2half_rn(krot);
+    const __half vh = __float2half_rn(vval);
+    a.kn[j] = __half2float(kh);
+    a.vn[j] = __half2float(vh);
+    // lanes j, j+1 pair up into one 32-bit device-scope store per row
+    const unsigned kbits = (unsigned)__half_as_ushort(kh), vbits = (unsigned)__half_as_ushort(vh);
+    const unsigned kpart = (unsigned)__shfl_xor((int)kbits, 1, 64);
+    const unsigned vpart = (unsigned)__shfl_xor((int)vbits, 1, 64);
+    if ((j & 1) == 0) {
+      unsigned* kc32 = reinterpret_cast<unsigned*>(p.kc + hb + (size_t)pos * hd);
+      unsigned* vc32 = reinterpret_cast<unsigned*>(p.vc + hb + (size_t)pos * hd);
+      st_cu(kc32 + (j >> 1), kbits | (kpart << 16));
+      st_cu(vc32 + (j >> 1), vbits | (vpart << 16));
     }
   }
   __syncthreads();
@@ -727,7 +1023,7 @@ __device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qr[h][e] = lane_on ? qs[h * hd + sub * 8 + e] : 0.f;
+    for (int e = 0; e < 8; ++e) qr[h][e] = lane_on ? a.qs[h * hd + sub * 8 + e] : 0.f;
 
   float m[G], lsum[G], acc[G][8];
 #pragma unroll
@@ -774,8 +1070,8 @@ __device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const
     float kf[8], vf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kf[e] = lane_on ? kn[sub * 8 + e] : 0.f;
-      vf[e] = lane_on ? vn[sub * 8 + e] : 0.f;
+      kf[e] = lane_on ? a.kn[sub * 8 + e] : 0.f;
+      vf[e] = lane_on ? a.vn[sub * 8 + e] : 0.f;
     }
     // only lanes 0..15 take part: the 16-lane sum stays inside the group
     consume(kf, vf);
@@ -789,21 +1085,21 @@ __device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const
       const float mo = __shfl_xor(m[h], o, 64);
       const float lo = __shfl_xor(lsum[h], o, 64);
       const float mn = fmaxf(m[h], mo);
-      const float a = exp2f(m[h] - mn), b = exp2f(mo - mn);
-      lsum[h] = lsum[h] * a + lo * b;
+      const float e0 = exp2f(m[h] - mn), e1 = exp2f(mo - mn);
+      lsum[h] = lsum[h] * e0 + lo * e1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float ao = __shfl_xor(acc[h][e], o, 64);
-        acc[h][e] = acc[h][e] * a + ao * b;
+        acc[h][e] = acc[h][e] * e0 + ao * e1;
       }
       m[h] = mn;
     }
   }
-  const int wstride = hd + 2;
+  const int ws = hd + 2;
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* st = wst + ((size_t)wave * G + h) * wstride;
+      float* st = a.wst + (wave * G + h) * ws;
       if (lane_on)
 #pragma unroll
         for (int e = 0; e < 8; ++e) st[sub * 8 + e] = acc[h][e];
@@ -814,73 +1110,71 @@ __device__ __forceinline__ void attn_unit(const Params& p, int l, int pos, const
     }
   }
   __syncthreads();
-  // merge the waves in order and write this split's partial
+  // merge the waves in order: this split's partial (or o itself when S == 1)
+  const unsigned fp = ll_flag(p, step, l, kSlotPart);
+  const unsigned fo = ll_flag(p, step, l, kSlotO);
   for (int t = threadIdx.x; t < G * hd; t += kThreads) {
     const int h = t / hd, i = t % hd;
     float M = kNegBig;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wst[((size_t)w * G + h) * wstride + hd]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, a.wst[(w * G + h) * ws + hd]);
     float Ls = 0.f, A = 0.f;
     for (int w = 0; w < kWaves; ++w) {
-      const float* st = wst + ((size_t)w * G + h) * wstride;
+      const float* st = a.wst + (w * G + h) * ws;
       const float sc = exp2f(st[hd] - M);
       Ls = fmaf(st[hd + 1], sc, Ls);
       A = fmaf(st[i], sc, A);
     }
-    float* out = p.part + ((size_t)(g * G + h) * S + sidx) * wstride;
-    st_c(out + i, A);
-    if (i == 0) {
-      st_c(out + hd, M);
-      st_c(out + hd + 1, Ls);
+    if (S == 1) {
+      ll_put(p, p.off_o + (g * G + h) * hd + i, A / Ls, fo);
+    } else {
+      ll_put(p, part_word(p, g, G, sidx, h, i), A, fp);
+      if (i == 0) {
+        ll_put(p, part_word(p, g, G, sidx, h, hd), M, fp);
+        ll_put(p, part_word(p, g, G, sidx, h, hd + 1), Ls, fp);
+      }
     }
   }
-  // publish the partial, count the arrival; the last split merges
-  wait_stores();
-  __builtin_amdgcn_s_barrier();
-  if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(p.head_ctr + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (old == (unsigned)(S - 1));
-    if (last) st_cu(p.head_ctr + g, 0u);
-    *flag = last;
+  if (kMerge && S > 1 && sidx == 0) {
+    __syncthreads();
+    return attn_gather_merge<G>(p, step, l, g, lds, c);
   }
-  __syncthreads();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (!*flag) return;
-  for (int t = threadIdx.x; t < G * hd; t += kThreads) {
-    const int h = t / hd, i = t % hd;
-    const float* pp = p.part + (size_t)(g * G + h) * S * wstride;
-    float M = kNegBig;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ld_c(pp + (size_t)s * wstride + hd));
-    float Ls = 0.f, A = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* st = pp + (size_t)s * wstride;
-      const float sc = exp2f(ld_c(st + hd) - M);
-      Ls = fmaf(ld_c(st + hd + 1), sc, Ls);
-      A = fmaf(ld_c(st + i), sc, A);
-    }
-    st_c(p.o + (size_t)(g * G + h) * hd + i, A / Ls);
-  }
+  return true;
 }
 
 // Units wg, wg + n_wg, ... of this workgroup (one unit unless the grid is
-// smaller than the number of KV heads); `pre` holds the first unit's first
-// cache rows when kPre.
-template <int G, bool kPre>
-__device__ __forceinline__ void stage_attn(const Params& p, int l, int pos, int wg, Lds s, int* flag,
-                                           KVPre pre) {
+// smaller than the number of KV heads, in which case there is one split per
+// head and no merge); `pre` holds the first unit's first cache rows.
+template <int G, bool kPre, bool kMerge>
+__device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int pos, int wg, Lds s,
+                                           KVPre pre, const Ctl& c, Tracer& tr) {
   const int units = p.nkv * p.splits;
-  if (wg >= units) return;
-  attn_unit<G, kPre>(p, l, pos, attn_unit_of(p, pos, wg), s.h, flag, pre);
+  if (wg >= units) {
+    mark(tr);
+    return true;
+  }
+  if (!attn_unit<G, kPre, kMerge>(p, step, l, pos, attn_unit_of(p, pos, wg), s.h, pre, c, tr))
+    return false;
   __syncthreads();
   for (int u = wg + p.n_wg; u < units; u += p.n_wg) {
-    attn_unit<G, false>(p, l, pos, attn_unit_of(p, pos, u), s.h, flag, KVPre{});
+    Tracer none{nullptr, 0};
+    if (!attn_unit<G, false, kMerge>(p, step, l, pos, attn_unit_of(p, pos, u), s.h, KVPre{}, c, none))
+      return false;
     __syncthreads();
   }
+  return true;
+}
+
+// Staged mode: merge kernel body (split 0 of each head group merges).
+template <int G>
+__device__ __forceinline__ bool stage_merge(const Params& p, int step, int l, int wg, Lds s, const Ctl& c) {
+  if (p.splits <= 1 || wg >= p.nkv) return true;
+  return attn_gather_merge<G>(p, step, l, wg, s.h, c);
 }
 
 // ---------------------------------------------------------------------------
-// Stage: O GEMV + residual.  Rows of x are owned by the same workgroup in
-// this stage and in the down stage.
+// Residual stages.  A workgroup owns the same rows [r0, r1) of x in the O
+// and down projections; it reads its own previous x rows from the arena
+// together with the stage input.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ GemvWork o_work(const Params& p, int wg) {
   return gemv_work(p.d, p.H * p.hd, p.n_wg, wg, false);
@@ -892,20 +1186,27 @@ __device__ __forceinline__ WPre prefetch_o(const Params& p, int l, int wg) {
   return gemv_prefetch(o_work(p, wg), o_addr(p, l));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_oproj(const Params& p, int l, const __half* emb_row, int wg, Lds s,
-                                            WPre pre) {
+__device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, const __half* emb_row,
+                                            int wg, Lds s, WPre pre, const Ctl& c, Tracer& tr) {
+  const GemvWork g = o_work(p, wg);
   const int qd = p.H * p.hd;
-  copy_to_lds(p.o, qd, s.h);
-  float* x = p.x;
-  const bool first = (l == 0);
-  gemv_run<kPre>(o_work(p, wg), o_addr(p, l), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) {
-               const int r = b0 + i;
-               const float xr = first ? __half2float(emb_row[r]) : ld_c(x + r);
-               st_c(x + r, xr + sums[i]);
-             }
-           });
+  const int nown = g.r1 - g.r0;
+  if (l == 0) {
+    for (int i = threadIdx.x; i < nown; i += kThreads) s.xown[i] = __half2float(emb_row[g.r0 + i]);
+  }
+  const LLRange rg[2] = {{p.off_o, qd, s.h, ll_flag(p, step, l, kSlotO)},
+                         {p.off_x + g.r0, l == 0 ? 0 : nown, s.xown,
+                          l == 0 ? 0u : ll_flag(p, step, l - 1, kSlotXDown)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
+  const unsigned f = ll_flag(p, step, l, kSlotXO);
+  gemv_run<kPre>(g, o_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const int r = b0 + i;
+      ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
+    }
+  });
+  return true;
 }
 
 // Stage: RMSNorm + paired gate/up GEMV + SwiGLU (dense FFN).
@@ -917,22 +1218,31 @@ __device__ __forceinline__ GemvWork gu_work(const Params& p, int wg) {
 }
 __device__ __forceinline__ PairAddr gu_addr(const Params& p, int l) {
   const LayerPtrs& w = p.layers[l];
-  return PairAddr{mat_rsrc(w.w_gate, p.F, p.d), mat_rsrc(w.w_up, p.F, p.d), p.d};
+  return PairAddr{w.w_gate, w.w_up, p.F, p.d};
 }
 __device__ __forceinline__ WPre prefetch_gateup(const Params& p, int l, int wg) {
-  const LayerPtrs& w = p.layers[l];
   return gemv_prefetch(gu_work(p, wg), gu_addr(p, l));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_gateup(const Params& p, int l, int wg, Lds s, WPre pre) {
-  const LayerPtrs& w = p.layers[l];
-  rmsnorm_to_lds(p, p.x, nullptr, w.ffn_norm, s.h, s.red);
-  float* u = p.u;
-  gemv_run<kPre>(gu_work(p, wg), gu_addr(p, l), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; 2 * i < n; i += kThreads)
-               st_c(u + (b0 >> 1) + i, silu(sums[2 * i]) * sums[2 * i + 1]);
-           });
+__device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+                                             const Ctl& c, Tracer& tr) {
+  const GemvWork g = gu_work(p, wg);
+  if (g.r0 >= g.r1) {
+    mark(tr);
+    return true;
+  }
+  const __half* gain = p.layers[l].ffn_norm;
+  const GainPre G = gain_prefetch(gain, p.d);
+  const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
+  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const unsigned f = ll_flag(p, step, l, kSlotU);
+  gemv_run<kPre>(g, gu_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+    for (int i = threadIdx.x; 2 * i < n; i += kThreads)
+      ll_put(p, p.off_u + (b0 >> 1) + i, silu(sums[2 * i]) * sums[2 * i + 1], f);
+  });
+  return true;
 }
 
 // Stage: down GEMV + residual (dense FFN).
@@ -946,19 +1256,28 @@ __device__ __forceinline__ WPre prefetch_down(const Params& p, int l, int wg) {
   return gemv_prefetch(down_work(p, wg), down_addr(p, l));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_down(const Params& p, int l, int wg, Lds s, WPre pre) {
-  copy_to_lds(p.u, p.F, s.h);
-  float* x = p.x;
-  gemv_run<kPre>(down_work(p, wg), down_addr(p, l), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) st_c(x + b0 + i, ld_c(x + b0 + i) + sums[i]);
-           });
+__device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+                                           const Ctl& c, Tracer& tr) {
+  const GemvWork g = down_work(p, wg);
+  const int nown = g.r1 - g.r0;
+  const LLRange rg[2] = {{p.off_u, p.F, s.h, ll_flag(p, step, l, kSlotU)},
+                         {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
+  const unsigned f = ll_flag(p, step, l, kSlotXDown);
+  gemv_run<kPre>(g, down_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const int r = b0 + i;
+      ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
+    }
+  });
+  return true;
 }
 
 // ---------------------------------------------------------------------------
-// MoE stages.  Router logits are computed by a few workgroups; after the
-// barrier every workgroup derives the same routing (softmax, top-k with the
-// lower id on ties) from them, so routing costs one barrier, not two.
+// MoE stages.  A few workgroups compute the router logits; every workgroup
+// then derives the same routing (softmax, top-k with the lower id on ties)
+// from them.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ GemvWork router_work(const Params& p, int wg) {
   return gemv_work(p.E, p.d, p.n_wg, wg, false);
@@ -970,24 +1289,31 @@ __device__ __forceinline__ WPre prefetch_router(const Params& p, int l, int wg) 
   return gemv_prefetch(router_work(p, wg), router_addr(p, l));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_router(const Params& p, int l, int wg, Lds s, WPre pre) {
+__device__ __forceinline__ bool stage_router(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+                                             const Ctl& c, Tracer& tr) {
   const GemvWork g = router_work(p, wg);
-  if (g.r0 >= g.r1) return;
-  rmsnorm_to_lds(p, p.x, nullptr, p.layers[l].ffn_norm, s.h, s.red);
-  float* out = p.router_logits;
-  gemv_run<kPre>(g, router_addr(p, l), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) st_c(out + b0 + i, sums[i]);
-           });
+  if (g.r0 >= g.r1) {
+    mark(tr);
+    return true;
+  }
+  const __half* gain = p.layers[l].ffn_norm;
+  const GainPre G = gain_prefetch(gain, p.d);
+  const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
+  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const unsigned f = ll_flag(p, step, l, kSlotRouter);
+  gemv_run<kPre>(g, router_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+    for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_router + b0 + i, sums[i], f);
+  });
+  return true;
 }
 
-// Routing in LDS: ids[a], wts[a] for the active slots a < topk + nshared
-// (routed experts in rank order, then the shared experts with weight 1).
-// `rl` is LDS scratch for the E router logits.
-__device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wts, float* rl) {
+// Routing in LDS from the router logits in `rl` (LDS): ids[a], wts[a] for
+// the active slots a < topk + nshared (routed experts in rank order, then
+// the shared experts with weight 1).
+__device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wts, const float* rl) {
   const int E = p.E, K = p.topk;
-  for (int e = threadIdx.x; e < E; e += kThreads) rl[e] = ld_c(p.router_logits + e);
-  __syncthreads();
   float mx = kNegBig;
   for (int e = 0; e < E; ++e) mx = fmaxf(mx, rl[e]);   // same order in every thread
   float den = 0.f;
@@ -1020,27 +1346,34 @@ __device__ __forceinline__ GemvWork moe_gu_work(const Params& p, int wg) {
   g.r1 *= 2;
   return g;
 }
-__device__ __forceinline__ void stage_moe_gateup(const Params& p, int l, int step, int wg, Lds s) {
+__device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int l, int wg, Lds s,
+                                                 const Ctl& c, Tracer& tr) {
   const LayerPtrs& w = p.layers[l];
   int* ids = moe_ids(s);
   float* wts = moe_wts(s);
+  const GemvWork g = moe_gu_work(p, wg);
+  const __half* gain = w.ffn_norm;
+  const GainPre G = gain_prefetch(gain, p.d);
+  const bool rows = g.r0 < g.r1;
+  const LLRange rg[2] = {{p.off_router, p.E, s.sums, ll_flag(p, step, l, kSlotRouter)},
+                         {p.off_x, rows ? p.d : 0, s.h, ll_flag(p, step, l, kSlotXO)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
   moe_routing(p, ids, wts, s.sums);
   if (p.mode == kDecode && wg == 0 && threadIdx.x < p.topk)
     p.expert_log[((size_t)step * p.L + l) * p.topk + threadIdx.x] = ids[threadIdx.x];
-  const GemvWork g = moe_gu_work(p, wg);
-  if (g.r0 >= g.r1) return;
-  rmsnorm_to_lds(p, p.x, nullptr, w.ffn_norm, s.h, s.red);
-  float* u = p.u;
-  const int Fe = p.Fe;
-  const int ne = p.E + p.nshared;
-  const MoePairAddr addr{mat_rsrc(w.e_gate, ne * Fe, p.d), mat_rsrc(w.e_up, ne * Fe, p.d), ids, Fe, p.d};
-  gemv_run<false>(g, addr, s.h, s.part, s.sums,
-           WPre{}, [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; 2 * i < n; i += kThreads) {
-               const int f = (b0 >> 1) + i;
-               st_c(u + f, wts[f / Fe] * silu(sums[2 * i]) * sums[2 * i + 1]);
-             }
-           });
+  if (!rows) return true;
+  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const int Fe = p.Fe, ne = p.E + p.nshared;
+  const MoePairAddr addr{w.e_gate, w.e_up, ids, ne, Fe, p.d};
+  const unsigned f = ll_flag(p, step, l, kSlotU);
+  gemv_run<false>(g, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
+    for (int i = threadIdx.x; 2 * i < n; i += kThreads) {
+      const int ff = (b0 >> 1) + i;
+      ll_put(p, p.off_u + ff, wts[ff / Fe] * silu(sums[2 * i]) * sums[2 * i + 1], f);
+    }
+  });
+  return true;
 }
 
 // Down projection of all active experts as one GEMV whose row r is the
@@ -1057,15 +1390,26 @@ __device__ __forceinline__ WPre prefetch_moe_down(const Params& p, int l, int wg
   return gemv_prefetch(moe_down_work(p, wg), moe_down_addr(p, l, s));
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_moe_down(const Params& p, int l, int wg, Lds s, WPre pre,
-                                               bool have_routing) {
+__device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+                                               bool have_routing, const Ctl& c, Tracer& tr) {
+  const GemvWork g = moe_down_work(p, wg);
+  const int nown = g.r1 - g.r0;
+  const int A = p.topk + p.nshared;
+  const LLRange rg[3] = {{p.off_u, A * p.Fe, s.h, ll_flag(p, step, l, kSlotU)},
+                         {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)},
+                         {p.off_router, have_routing ? 0 : p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
   if (!have_routing) moe_routing(p, moe_ids(s), moe_wts(s), s.sums);
-  copy_to_lds(p.u, (p.topk + p.nshared) * p.Fe, s.h);
-  float* x = p.x;
-  gemv_run<kPre>(moe_down_work(p, wg), moe_down_addr(p, l, s), s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) st_c(x + b0 + i, ld_c(x + b0 + i) + sums[i]);
-           });
+  const unsigned f = ll_flag(p, step, l, kSlotXDown);
+  gemv_run<kPre>(g, moe_down_addr(p, l, s), s.h, s.part, s.sums, pre,
+                 [&](int b0, int n, const float* sums) {
+                   for (int i = threadIdx.x; i < n; i += kThreads) {
+                     const int r = b0 + i;
+                     ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
+                   }
+                 });
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -1080,19 +1424,29 @@ __device__ __forceinline__ WPre prefetch_lmhead(const Params& p, int wg) {
   return gemv_prefetch(lm_work(p, wg), RowAddr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d});
 }
 template <bool kPre>
-__device__ __forceinline__ void stage_lmhead(const Params& p, int step, int wg, Lds s, WPre pre) {
-  rmsnorm_to_lds(p, p.x, nullptr, p.final_norm, s.h, s.red);
+__device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, Lds s, WPre pre,
+                                             const Ctl& c, Tracer& tr) {
+  const GemvWork g = lm_work(p, wg);
+  if (g.r0 >= g.r1) {
+    mark(tr);
+    return true;
+  }
+  const GainPre G = gain_prefetch(p.final_norm, p.d);
+  const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, p.L - 1, kSlotXDown)}};
+  if (!ll_gather(p, rg, c)) return false;
+  mark(tr);
+  rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
   float* logits = p.out_logits ? p.out_logits + (size_t)step * p.Vout : nullptr;
   unsigned long long best = 0ull;
-  gemv_run<kPre>(lm_work(p, wg), RowAddr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d}, s.h, s.part, s.sums, pre,
-           [&](int b0, int n, const float* sums) {
-             for (int i = threadIdx.x; i < n; i += kThreads) {
-               const float v = sums[i];
-               if (logits) logits[b0 + i] = v;
-               const unsigned long long k = argmax_key(v, b0 + i);
-               best = k > best ? k : best;
-             }
-           });
+  gemv_run<kPre>(g, RowAddr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d}, s.h, s.part, s.sums, pre,
+                 [&](int b0, int n, const float* sums) {
+                   for (int i = threadIdx.x; i < n; i += kThreads) {
+                     const float v = sums[i];
+                     if (logits) logits[b0 + i] = v;
+                     const unsigned long long k = argmax_key(v, b0 + i);
+                     best = k > best ? k : best;
+                   }
+                 });
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long other = __shfl_xor(best, o, 64);
     best = other > best ? other : best;
@@ -1107,11 +1461,14 @@ __device__ __forceinline__ void stage_lmhead(const Params& p, int step, int wg, 
     if (b != 0ull)
       __hip_atomic_fetch_max(p.amax + (step & 1), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
-// The persistent kernel.  Per barrier: arrive, issue the next stage's first
-// loads, wait.
+// The persistent kernel.  Each stage issues the next stage's first weight
+// (or KV) loads as soon as it has stored its own outputs, then waits only
+// for the activations it consumes.  One grid barrier per step publishes the
+// argmax (decode) or orders prefill steps.
 // ---------------------------------------------------------------------------
 // The parameter block lives in device memory and is re-read (scalar loads,
 // scalar-cache hits) at every stage: `fresh` hides the pointer from the
@@ -1131,6 +1488,8 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   const int wg = blockIdx.x;
   GridSync gs;
   Lds s;
+  Ctl c;
+  Tracer tr{nullptr, 0};
   int tok, n_steps, L, pos0, trace_step;
   bool moe, decode;
   unsigned long long* trace;
@@ -1138,6 +1497,7 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
     const Params& p = fresh(pp);
     s = lds_carve(p, smem);
     gs = make_sync(p.bar, p.err, (unsigned)p.n_wg, p.timeout_ticks, p.spin_limit);
+    c = make_ctl(p, &flag);
     moe = p.E != 0;
     decode = p.mode == kDecode;
     n_steps = p.n_steps;
@@ -1150,59 +1510,50 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   WPre wpre = prefetch_qkv(fresh(pp), 0, wg);
   for (int step = 0; step < n_steps; ++step) {
     const int pos = pos0 + step;
-    gs.tr = (step == trace_step) ? trace : nullptr;
-    gs.ev = 0;
-    trace_mark(gs);
+    tr.tr = (step == trace_step) ? trace : nullptr;
+    tr.ev = 0;
+    mark(tr);
     for (int l = 0; l < L; ++l) {
       {
         const Params& p = fresh(pp);
-        stage_qkv<true>(p, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre);
+        if (!stage_qkv<true>(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre, c, tr)) return;
       }
-      grid_arrive(gs);
+      mark(tr);
       const KVPre kvpre = prefetch_attn(fresh(pp), l, pos, wg);
-      if (!grid_wait(gs, &flag)) return;
-      stage_attn<G, true>(fresh(pp), l, pos, wg, s, &flag, kvpre);
-      grid_arrive(gs);
+      if (!stage_attn<G, true, true>(fresh(pp), step, l, pos, wg, s, kvpre, c, tr)) return;
+      mark(tr);
       wpre = prefetch_o(fresh(pp), l, wg);
-      if (!grid_wait(gs, &flag)) return;
       {
         const Params& p = fresh(pp);
-        stage_oproj<true>(p, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre);
+        if (!stage_oproj<true>(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre, c, tr)) return;
       }
-      grid_arrive(gs);
+      mark(tr);
       if (!moe) {
         wpre = prefetch_gateup(fresh(pp), l, wg);
-        if (!grid_wait(gs, &flag)) return;
-        stage_gateup<true>(fresh(pp), l, wg, s, wpre);
-        grid_arrive(gs);
+        if (!stage_gateup<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
+        mark(tr);
         wpre = prefetch_down(fresh(pp), l, wg);
-        if (!grid_wait(gs, &flag)) return;
-        stage_down<true>(fresh(pp), l, wg, s, wpre);
+        if (!stage_down<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
       } else {
         wpre = prefetch_router(fresh(pp), l, wg);
-        if (!grid_wait(gs, &flag)) return;
-        stage_router<true>(fresh(pp), l, wg, s, wpre);
-        grid_arrive(gs);
-        if (!grid_wait(gs, &flag)) return;
-        stage_moe_gateup(fresh(pp), l, step, wg, s);
-        grid_arrive(gs);
+        if (!stage_router<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
+        mark(tr);
+        if (!stage_moe_gateup(fresh(pp), step, l, wg, s, c, tr)) return;
+        mark(tr);
         wpre = prefetch_moe_down(fresh(pp), l, wg, s);
-        if (!grid_wait(gs, &flag)) return;
-        stage_moe_down<true>(fresh(pp), l, wg, s, wpre, true);
+        if (!stage_moe_down<true>(fresh(pp), step, l, wg, s, wpre, true, c, tr)) return;
       }
-      grid_arrive(gs);
-      if (l + 1 < L) {
-        wpre = prefetch_qkv(fresh(pp), l + 1, wg);
-        if (!grid_wait(gs, &flag)) return;
-      }
+      mark(tr);
+      if (l + 1 < L) wpre = prefetch_qkv(fresh(pp), l + 1, wg);
     }
     if (decode) {
       wpre = prefetch_lmhead(fresh(pp), wg);
-      if (!grid_wait(gs, &flag)) return;
-      stage_lmhead<true>(fresh(pp), step, wg, s, wpre);
+      if (!stage_lmhead<true>(fresh(pp), step, wg, s, wpre, c, tr)) return;
+      mark(tr);
       grid_arrive(gs);
       wpre = prefetch_qkv(fresh(pp), 0, wg);
       if (!grid_wait(gs, &flag)) return;
+      mark(tr);
       const Params& p = fresh(pp);
       tok = argmax_index(ld_c64(p.amax + (step & 1)), p.Vout);
       if (wg == 0 && threadIdx.x == 0) {
@@ -1210,6 +1561,8 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
         st_c64(p.amax + ((step + 1) & 1), 0ull);
       }
     } else {
+      // the next prefill step's first attention reads this step's KV rows
+      grid_arrive(gs);
       wpre = prefetch_qkv(fresh(pp), 0, wg);
       if (!grid_wait(gs, &flag)) return;
       tok = fresh(pp).prompt[step + 1];
@@ -1221,34 +1574,45 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   }
 }
 
-// ---- staged mode: one kernel per stage, the step counter lives on device
-enum StageId : int { kSQkv, kSAttn, kSO, kSGateUp, kSDown, kSRouter, kSMoeGateUp, kSMoeDown, kSLm };
+// ---- staged mode: one kernel per stage, the step counter lives on device.
+// Kernel boundaries order the stages, so every wait for activations is
+// satisfied at its first read.
+enum StageId : int { kSQkv, kSAttn, kSMerge, kSO, kSGateUp, kSDown, kSRouter, kSMoeGateUp, kSMoeDown, kSLm };
 
 __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage, int l) {
   extern __shared__ float smem[];
   __shared__ int flag;
   const Lds s = lds_carve(p, smem);
+  const Ctl c = make_ctl(p, &flag);
   const int wg = blockIdx.x;
   const int step = p.state[1];
   const int pos = p.pos0 + step;
   const int tok = (p.mode == kPrefill) ? p.prompt[step] : p.state[0];
   const __half* emb = p.tok_emb + (size_t)tok * p.d;
+  Tracer none{nullptr, 0};
   switch (stage) {
-    case kSQkv: stage_qkv<false>(p, l, emb, wg, s, WPre{}); break;
+    case kSQkv: (void)stage_qkv<false>(p, step, l, emb, wg, s, WPre{}, c, none); break;
     case kSAttn:
       switch (p.H / p.nkv) {
-        case 1: stage_attn<1, false>(p, l, pos, wg, s, &flag, KVPre{}); break;
-        case 2: stage_attn<2, false>(p, l, pos, wg, s, &flag, KVPre{}); break;
-        default: stage_attn<4, false>(p, l, pos, wg, s, &flag, KVPre{}); break;
+        case 1: (void)stage_attn<1, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
+        case 2: (void)stage_attn<2, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
+        default: (void)stage_attn<4, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
       }
       break;
-    case kSO: stage_oproj<false>(p, l, emb, wg, s, WPre{}); break;
-    case kSGateUp: stage_gateup<false>(p, l, wg, s, WPre{}); break;
-    case kSDown: stage_down<false>(p, l, wg, s, WPre{}); break;
-    case kSRouter: stage_router<false>(p, l, wg, s, WPre{}); break;
-    case kSMoeGateUp: stage_moe_gateup(p, l, step, wg, s); break;
-    case kSMoeDown: stage_moe_down<false>(p, l, wg, s, WPre{}, false); break;
-    case kSLm: stage_lmhead<false>(p, step, wg, s, WPre{}); break;
+    case kSMerge:
+      switch (p.H / p.nkv) {
+        case 1: (void)stage_merge<1>(p, step, l, wg, s, c); break;
+        case 2: (void)stage_merge<2>(p, step, l, wg, s, c); break;
+        default: (void)stage_merge<4>(p, step, l, wg, s, c); break;
+      }
+      break;
+    case kSO: (void)stage_oproj<false>(p, step, l, emb, wg, s, WPre{}, c, none); break;
+    case kSGateUp: (void)stage_gateup<false>(p, step, l, wg, s, WPre{}, c, none); break;
+    case kSDown: (void)stage_down<false>(p, step, l, wg, s, WPre{}, c, none); break;
+    case kSRouter: (void)stage_router<false>(p, step, l, wg, s, WPre{}, c, none); break;
+    case kSMoeGateUp: (void)stage_moe_gateup(p, step, l, wg, s, c, none); break;
+    case kSMoeDown: (void)stage_moe_down<false>(p, step, l, wg, s, WPre{}, false, c, none); break;
+    case kSLm: (void)stage_lmhead<false>(p, step, wg, s, WPre{}, c, none); break;
   }
 }
 
@@ -1274,12 +1638,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_kernel(const __half* w, cons
   float* h = smem;
   float* part = smem + ((cols + 63) & ~63);
   float* sums = part + kPartCap;
-  copy_to_lds(x, cols, h);
+  for (int i = threadIdx.x; i < cols; i += kThreads) h[i] = x[i];
+  __syncthreads();
   gemv_run<false>(gemv_work(rows, cols, n_wg, blockIdx.x, false), RowAddr{mat_rsrc(w, rows, cols), cols},
-                  h, part, sums,
-           WPre{}, [&](int b0, int n, const float* sm) {
-             for (int i = threadIdx.x; i < n; i += kThreads) y[b0 + i] = sm[i];
-           });
+                  h, part, sums, WPre{}, [&](int b0, int n, const float* sm) {
+                    for (int i = threadIdx.x; i < n; i += kThreads) y[b0 + i] = sm[i];
+                  });
 }
 
 __global__ __launch_bounds__(kThreads, 1) void barrier_test_kernel(unsigned* bar, unsigned* slots,
@@ -1372,6 +1736,7 @@ hipError_t launch_staged_step(const Params& p, size_t lds_bytes, hipStream_t s) 
   for (int l = 0; l < p.L; ++l) {
     hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSQkv, l);
     hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSAttn, l);
+    if (p.splits > 1) hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSMerge, l);
     hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSO, l);
     if (p.E == 0) {
       hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSGateUp, l);

@@ -48,14 +48,16 @@ struct Params {
   __half* vc;                   // [L][nkv][cap][hd]
   const float* rope_cos;        // [cap][hd/2]
   const float* rope_sin;        // [cap][hd/2]
-  float* x;                     // [d]      residual stream
-  float* qkv;                   // [H*hd + 2*nkv*hd]
-  float* o;                     // [H*hd]   attention output (head-major)
-  float* u;                     // [max(F, (topk+nshared)*Fe)]  FFN hidden
-  float* part;                  // [H][splits][hd+2]  split-K partial (acc, m, l)
-  float* router_logits;         // [E]
+  unsigned long long* act;      // activation arena: 64-bit words (epoch << 32 | fp32 bits)
+  int act_words;
+  int off_x;                    // [d]            residual stream
+  int off_qkv;                  // [H*hd + 2*nkv*hd]
+  int off_o;                    // [H*hd]         attention output (head-major)
+  int off_u;                    // [max(F, (topk+nshared)*Fe)]  FFN hidden
+  int off_router;               // [E]            router logits
+  int off_part;                 // [nkv][splits][G][hd+2]  split-K partials (acc, m, l)
+  unsigned epoch0;              // epoch of (step 0, layer 0, slot 0) of this launch
   unsigned* bar;                // grid barrier counters [kBarrierWords]
-  unsigned* head_ctr;           // [nkv] split arrivals per KV head
   unsigned long long* amax;     // [2] packed (logit, index) argmax slots
   int* err;                     // device error word (0 = ok)
   int* state;                   // [0] pending token, [1] graph-mode step counter
@@ -90,14 +92,17 @@ hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, uns
 
 // Dynamic LDS layout (in floats) shared by host and device:
 //   [0, hcap)               GEMV input vector (largest GEMV input length) or
-//                           the attention unit's q / new-KV / per-wave state
+//                           the attention unit's q / new K,V / per-wave state
+//                           / the split partials it merges
 //   [part_off, +kPartCap)   GEMV per-task partials of one row block
 //   [sums_off, +kPartCap)   GEMV row sums of one row block; MoE router logits
+//   [xown_off, +kPartCap)   this workgroup's rows of the residual stream
 //   [red_off, +kRedFloats)  reductions, argmax keys, MoE routing
 struct LdsLayout {
   int hcap;
   int part_off;
   int sums_off;
+  int xown_off;
   int red_off;
   int total;
 };
@@ -113,13 +118,15 @@ __host__ __device__ inline LdsLayout lds_layout(const Params& p) {
   else v = v > moe_in ? v : moe_in;
   const int G = p.H / p.nkv;
   const int gpad = G <= 1 ? 1 : G <= 2 ? 2 : 4;
-  const int attn = gpad * p.hd + 2 * p.hd + kWaves * gpad * (p.hd + 2);
+  const int S = p.splits > 1 ? p.splits : 1;
+  const int attn = gpad * p.hd + 2 * p.hd + (kWaves + S) * gpad * (p.hd + 2);
   v = v > attn ? v : attn;
   LdsLayout L;
   L.hcap = (v + 63) & ~63;
   L.part_off = L.hcap;
   L.sums_off = L.part_off + kPartCap;
-  L.red_off = L.sums_off + kPartCap;
+  L.xown_off = L.sums_off + kPartCap;
+  L.red_off = L.xown_off + kPartCap;
   L.total = L.red_off + kRedFloats;
   return L;
 }

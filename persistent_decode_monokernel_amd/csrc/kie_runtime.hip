@@ -98,6 +98,7 @@ struct kie_handle {
   bool broken = false;
   int last_decode_steps = 0;
   int trace_events = 0;          // events per workgroup recorded by the last decode
+  unsigned epoch_next = 1;       // first activation epoch of the next launch
 };
 
 namespace {
@@ -126,7 +127,6 @@ void free_handle(kie_handle* h) {
 int reset_sync_words(kie_handle* h) {
   const kie::Params& b = h->base;
   KIE_HIP(hipMemsetAsync(b.bar, 0, sizeof(unsigned) * kie::kBarrierWords, h->stream));
-  KIE_HIP(hipMemsetAsync(b.head_ctr, 0, sizeof(unsigned) * b.nkv, h->stream));
   KIE_HIP(hipMemsetAsync(b.amax, 0, 2 * sizeof(unsigned long long), h->stream));
   KIE_HIP(hipMemsetAsync(b.err, 0, sizeof(int), h->stream));
   KIE_HIP(hipMemsetAsync(b.state + 1, 0, sizeof(int), h->stream));
@@ -148,10 +148,26 @@ int finish_launch(kie_handle* h) {
   return KIE_OK;
 }
 
+// Gives the launch a fresh range of activation epochs: every stage of every
+// step of this launch stamps its outputs with an epoch no earlier launch
+// used, so stale arena words never satisfy a wait.  When the 32-bit range
+// would run out, the arena is cleared and numbering restarts.
+int assign_epochs(kie_handle* h, kie::Params& p) {
+  const unsigned long long need = (unsigned long long)(p.n_steps + 1) * p.L * 8ull + 8ull;
+  if ((unsigned long long)h->epoch_next + need >= 0xFFFFFF00ull) {
+    KIE_HIP(hipMemsetAsync(h->base.act, 0, sizeof(unsigned long long) * h->base.act_words, h->stream));
+    h->epoch_next = 1;
+  }
+  p.epoch0 = h->epoch_next;
+  h->epoch_next += (unsigned)need;
+  return KIE_OK;
+}
+
 // Runs p.n_steps steps (prefill or decode) in the handle's mode.
 int run_steps(kie_handle* h, kie::Params& p) {
   int rc = reset_sync_words(h);
   if (rc) return rc;
+  if ((rc = assign_epochs(h, p))) return rc;
   const bool staged = (h->cfg.flags & KIE_MODE_GRAPH) != 0;
   if (!staged) {
     h->call = p;
@@ -241,6 +257,10 @@ int kie_config_check(const kie_config* c) {
   if (c->n_workgroups < 0 || c->n_workgroups > 4096) return fail(KIE_ERR_INVALID_ARG, "n_workgroups out of range");
   if (c->timeout_ms < 0) return fail(KIE_ERR_INVALID_ARG, "timeout_ms < 0");
   kie::Params p = shape_params(*c);
+  // the LDS need grows with the attention splits, i.e. with the grid: check
+  // the configured grid, or 256 workgroups (one per MI355X compute unit)
+  p.n_wg = c->n_workgroups > 0 ? c->n_workgroups : 256;
+  p.splits = std::max(1, p.n_wg / p.nkv);
   const kie::LdsLayout L = kie::lds_layout(p);
   if ((size_t)L.total * sizeof(float) > kMaxLdsBytes)
     return fail(KIE_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
@@ -301,8 +321,13 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   p = shape_params(c);
   p.n_wg = c.n_workgroups > 0 ? c.n_workgroups : n_cu;
   p.splits = std::max(1, p.n_wg / p.nkv);
+  if ((c.d_model + p.n_wg - 1) / p.n_wg > kie::kPartCap)
+    return bail(fail(KIE_ERR_UNSUPPORTED, "d_model / n_workgroups must be at most " +
+                                              std::to_string(kie::kPartCap)));
   const kie::LdsLayout L = kie::lds_layout(p);
   h->lds = (size_t)L.total * sizeof(float);
+  if (h->lds > kMaxLdsBytes)
+    return bail(fail(KIE_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has"));
   const int per_cu = kie::max_blocks_per_cu(c.n_heads / c.n_kv_heads, h->lds);
   if (per_cu < 1 || (long long)per_cu * n_cu < p.n_wg)
     return bail(fail(KIE_ERR_OCCUPANCY, "grid of " + std::to_string(p.n_wg) +
@@ -329,16 +354,26 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   rc_tab = static_cast<float*>(ptr);
   p.rope_cos = rc_tab;
   p.rope_sin = rc_tab + cap * (hd / 2);
-  KIE_ALLOC(x, float, d);
-  KIE_ALLOC(qkv, float, qd + 2 * kd);
-  KIE_ALLOC(o, float, qd);
+  // activation arena (64-bit flag-in-data words), one region per buffer
   const size_t ucount = c.n_experts ? (size_t)(c.top_k + c.n_shared_experts) * c.expert_hidden
                                     : (size_t)c.ffn_hidden;
-  KIE_ALLOC(u, float, ucount);
-  KIE_ALLOC(part, float, (size_t)c.n_heads * p.splits * (hd + 2));
-  KIE_ALLOC(router_logits, float, std::max(1, c.n_experts));
+  {
+    size_t off = 0;
+    auto region = [&](int& field, size_t words) {
+      field = (int)off;
+      off += (words + 1) & ~(size_t)1;     // keep regions 16-byte aligned
+    };
+    region(p.off_x, d);
+    region(p.off_qkv, qd + 2 * kd);
+    region(p.off_o, qd);
+    region(p.off_u, ucount);
+    region(p.off_router, std::max(1, c.n_experts));
+    region(p.off_part, (size_t)c.n_heads * p.splits * (hd + 2));
+    if (off * 8 >= 0xFFFFFF00ull) return bail(fail(KIE_ERR_UNSUPPORTED, "activation arena too large"));
+    p.act_words = (int)off;
+    KIE_ALLOC(act, unsigned long long, off);
+  }
   KIE_ALLOC(bar, unsigned, kie::kBarrierWords);
-  KIE_ALLOC(head_ctr, unsigned, c.n_kv_heads);
   KIE_ALLOC(amax, unsigned long long, 2);
   KIE_ALLOC(err, int, 1);
   KIE_ALLOC(state, int, 4);
@@ -379,6 +414,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   if (hipMemcpy(h->d_layers, lp.data(), sizeof(kie::LayerPtrs) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(rc_tab, tab.data(), sizeof(float) * tab.size(), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemset(p.state, 0, 4 * sizeof(int)) != hipSuccess ||
+      hipMemset(p.act, 0, sizeof(unsigned long long) * (size_t)p.act_words) != hipSuccess ||
       hipEventCreate(&h->ev0) != hipSuccess || hipEventCreate(&h->ev1) != hipSuccess)
     return bail(fail(KIE_ERR_HIP, "initialising handle buffers failed"));
   const int tmo = c.timeout_ms > 0 ? c.timeout_ms : 20000;
@@ -439,9 +475,10 @@ int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits)
   h->last_decode_steps = n;
   if (p.trace) {
     const int per_layer = h->cfg.n_experts ? 6 : 5;
-    // step start, then arrive/leave for every barrier: per_layer per layer and
-    // one after the lm_head stage
-    h->trace_events = std::min(kie::kTraceEvents, 1 + 2 * (h->cfg.n_layers * per_layer + 1));
+    // step start; for every stage (per_layer per layer, then lm_head) the
+    // moment its inputs were complete and the moment it finished; the
+    // argmax barrier's release
+    h->trace_events = std::min(kie::kTraceEvents, 1 + 2 * (h->cfg.n_layers * per_layer + 1) + 1);
   }
   return KIE_OK;
 }
