@@ -86,9 +86,12 @@ def cpu_baseline(cfg, W, prompt, budget_s: float):
 def trace_summary(cfg, tr):
     """Per-stage timing of one traced decode step from the in-kernel clock
     stamps (100 MHz wall clock).  Each stage records when its inputs were
-    complete ("ready") and when it finished ("end"); "wait" is ready minus
-    the workgroup's previous end, "work" is end minus ready.  Reported per
-    stage kind: the mean over layers of the mean and max over workgroups."""
+    complete ("ready"), when its main loop started ("start", after the norm
+    or the RoPE and KV append) and when it finished ("end"); "wait" is ready
+    minus the workgroup's previous end, "prep" start minus ready, "work" end
+    minus start.  The first Q/K/V stage of a step also waits for the
+    previous step's argmax barrier.  Reported per stage kind: the mean over layers of the mean
+    and max over workgroups."""
     import numpy as np
     t = tr.astype(np.float64) * 10.0 / 1000.0          # ticks of 10 ns -> us
     t -= t[:, :1]
@@ -98,23 +101,21 @@ def trace_summary(cfg, tr):
     out = {}
     prev_end = t[:, 0]
     for k, name in enumerate(names):
-        if 2 + 2 * k >= t.shape[1]:
+        if 3 + 3 * k >= t.shape[1]:
             break
-        ready, end = t[:, 1 + 2 * k], t[:, 2 + 2 * k]
-        wait, work = ready - prev_end, end - ready
-        d = out.setdefault(name, {"n": 0, "wait_mean_us": 0.0, "wait_max_us": 0.0,
-                                  "work_mean_us": 0.0, "work_max_us": 0.0})
+        ready, start, end = t[:, 1 + 3 * k], t[:, 2 + 3 * k], t[:, 3 + 3 * k]
+        parts = {"wait": ready - prev_end, "prep": start - ready, "work": end - start}
+        d = out.setdefault(name, {"n": 0})
         d["n"] += 1
-        d["wait_mean_us"] += float(wait.mean())
-        d["wait_max_us"] += float(wait.max())
-        d["work_mean_us"] += float(work.mean())
-        d["work_max_us"] += float(work.max())
+        for key, v in parts.items():
+            d[key + "_mean_us"] = d.get(key + "_mean_us", 0.0) + float(v.mean())
+            d[key + "_max_us"] = d.get(key + "_max_us", 0.0) + float(v.max())
         prev_end = end
     for d in out.values():
-        for key in ("wait_mean_us", "wait_max_us", "work_mean_us", "work_max_us"):
-            d[key] /= d["n"]
-    barrier = float((t[:, -1] - prev_end).mean())
-    return {"step_us": float(t[:, -1].max()), "argmax_barrier_mean_us": barrier, "stages": out}
+        for key in list(d):
+            if key != "n":
+                d[key] /= d["n"]
+    return {"step_us": float(t[:, -1].max()), "stages": out}
 
 
 def hbm_probes(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 10) -> dict:

@@ -682,32 +682,44 @@ __device__ __forceinline__ void mark(Tracer& t) {
 // ---------------------------------------------------------------------------
 // Row address functors of each GEMV.
 // ---------------------------------------------------------------------------
+// Layer l's weight pointers, read through the constant address space so
+// they are scalar loads into SGPRs (a vector load would leave them in VGPRs,
+// and every later use would wait for all loads issued before it).
+typedef const __attribute__((address_space(4))) unsigned long long* ConstU64Ptr;
+__device__ __forceinline__ LayerPtrs layer(const Params& p, int l) {
+  constexpr int kWords = (int)(sizeof(LayerPtrs) / sizeof(unsigned long long));
+  const ConstU64Ptr q = (ConstU64Ptr)(p.layers + l);
+  unsigned long long v[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) v[i] = q[i];
+  return __builtin_bit_cast(LayerPtrs, v);
+}
+
 // A wave-uniform address as an opaque uniform value (readfirstlane of both
 // halves): keeps it in SGPRs and keeps the optimiser from folding a choice
 // between struct members into an indexed load of the struct.
-__device__ __forceinline__ uintptr_t uniform_addr(const void* p) {
+__device__ __forceinline__ unsigned long long uniform_addr(const void* p) {
   const unsigned long long v = (unsigned long long)(uintptr_t)p;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
-  return (uintptr_t)(((unsigned long long)hi << 32) | lo);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 // Each GEMV's weights as buffer resources: rsrc(r) is the resource holding
 // row r (uniform across the wave), off(r, c) the byte offset of 16-byte
 // chunk c of that row.  Every resource spans its whole tensor (< 4 GiB).
 struct QkvAddr {             // rows of Wq, then Wk, then Wv
-  const __half *wq, *wk, *wv;
+  unsigned long long bq, bk, bv;   // uniform base addresses (SGPRs)
   int qd, kd, d;
-  // The resource is built from a base pointer selected among opaque copies
-  // of the members: a select of the members themselves is folded into an
-  // indexed load from the functor, which then lives in scratch memory.
+  // The matrix is chosen by arithmetic on uniform values, not by branches or
+  // selects over the members (either would cost waits or scratch memory).
   __device__ Rsrc rsrc(int r) const {
-    const bool isq = r < qd, isk = !isq && r < qd + kd;
-    const uintptr_t b = isq ? uniform_addr(wq) : (isk ? uniform_addr(wk) : uniform_addr(wv));
-    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)(isq ? qd : kd) * d * 2);
+    const unsigned long long iq = r < qd, ik = (r >= qd) & (r < qd + kd), iv = r >= qd + kd;
+    const unsigned long long b = iq * bq + ik * bk + iv * bv;
+    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)(iq ? qd : kd) * d * 2);
   }
   __device__ unsigned off(int r, int c) const {
-    const int rr = r < qd ? r : (r < qd + kd ? r - qd : r - qd - kd);
+    const int rr = r - (r >= qd) * qd - (r >= qd + kd) * kd;
     return (unsigned)rr * (unsigned)d * 2u + (unsigned)c * 16u;
   }
 };
@@ -720,23 +732,23 @@ struct RowAddr {             // plain row-major [rows][cols]
   }
 };
 struct PairAddr {            // virtual row 2f = gate row f, 2f+1 = up row f
-  const __half *gate, *up;
+  unsigned long long bg, bu;       // uniform base addresses
   int rows, cols;
   __device__ Rsrc rsrc(int vr) const {
-    const uintptr_t b = (vr & 1) ? uniform_addr(up) : uniform_addr(gate);
-    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)rows * cols * 2);
+    const unsigned long long iu = vr & 1;
+    return make_rsrc(reinterpret_cast<const void*>((1ull - iu) * bg + iu * bu), (size_t)rows * cols * 2);
   }
   __device__ unsigned off(int vr, int c) const {
     return (unsigned)(vr >> 1) * (unsigned)cols * 2u + (unsigned)c * 16u;
   }
 };
 struct MoePairAddr {         // virtual row 2f (+1): pair f = (slot f / Fe, row f % Fe)
-  const __half *gate, *up;   // whole stacked expert tensors [E + S][Fe][d]
+  unsigned long long bg, bu;       // whole stacked expert tensors [E + S][Fe][d]
   const int* ids;            // LDS: expert id per active slot
   int ne, Fe, d;
   __device__ Rsrc rsrc(int vr) const {
-    const uintptr_t b = (vr & 1) ? uniform_addr(up) : uniform_addr(gate);
-    return make_rsrc(reinterpret_cast<const void*>(b), (size_t)ne * Fe * d * 2);
+    const unsigned long long iu = vr & 1;
+    return make_rsrc(reinterpret_cast<const void*>((1ull - iu) * bg + iu * bu), (size_t)ne * Fe * d * 2);
   }
   __device__ unsigned off(int vr, int c) const {
     const int f = vr >> 1;
@@ -768,33 +780,48 @@ __device__ __forceinline__ GemvWork qkv_work(const Params& p, int wg) {
   return gemv_work(p.H * p.hd + 2 * p.nkv * p.hd, p.d, p.n_wg, wg, false);
 }
 __device__ __forceinline__ QkvAddr qkv_addr(const Params& p, int l) {
-  const LayerPtrs& w = p.layers[l];
+  const LayerPtrs w = layer(p, l);
   const int qd = p.H * p.hd, kd = p.nkv * p.hd;
-  return QkvAddr{w.wq, w.wk, w.wv, qd, kd, p.d};
+  return QkvAddr{uniform_addr(w.wq), uniform_addr(w.wk), uniform_addr(w.wv), qd, kd, p.d};
 }
-__device__ __forceinline__ WPre prefetch_qkv(const Params& p, int l, int wg) {
-  return gemv_prefetch(qkv_work(p, wg), qkv_addr(p, l));
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, const __half* emb_row,
-                                          int wg, Lds s, WPre pre, const Ctl& c, Tracer& tr) {
+// Every stage first issues the first loads of its own weight rows (or KV
+// rows), then waits for its inputs: the loads stream while the workgroup
+// waits.  The issued batches stay in registers local to the stage.
+//
+// At layer 0 the input is the embedding row of the step's token; `resolve`
+// yields that token after the optional grid barrier `gs` (the previous
+// step's argmax, or prefill ordering) and is called by every workgroup.
+template <class Resolve>
+__device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int wg, Lds s,
+                                          const Ctl& c, Tracer& tr, GridSync& gs, bool wait_first,
+                                          int& tok, Resolve&& resolve) {
   const GemvWork g = qkv_work(p, wg);
-  if (g.r0 >= g.r1) {
-    mark(tr);
-    return true;
-  }
-  const __half* gain = p.layers[l].attn_norm;
+  const QkvAddr addr = qkv_addr(p, l);
+  const WPre pre = gemv_prefetch(g, addr);
+  const __half* gain = layer(p, l).attn_norm;
   const GainPre G = gain_prefetch(gain, p.d);
+  if (wait_first) {
+    if (!grid_wait(gs, c.flag)) return false;
+    tok = resolve();
+  }
   if (l == 0) {
-    for (int i = threadIdx.x; i < p.d; i += kThreads) s.h[i] = __half2float(emb_row[i]);
-  } else {
+    if (g.r0 < g.r1) {
+      const __half* emb_row = p.tok_emb + (size_t)tok * p.d;
+      for (int i = threadIdx.x; i < p.d; i += kThreads) s.h[i] = __half2float(emb_row[i]);
+    }
+  } else if (g.r0 < g.r1) {
     const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l - 1, kSlotXDown)}};
     if (!ll_gather(p, rg, c)) return false;
   }
   mark(tr);
+  if (g.r0 >= g.r1) {
+    mark(tr);
+    return true;
+  }
   rmsnorm_lds(p, gain, G, s.h, s.red);
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotQkv);
-  gemv_run<kPre>(g, qkv_addr(p, l), s.h, s.part, s.sums, pre,
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
                    for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_qkv + b0 + i, sums[i], f);
                  });
@@ -1013,6 +1040,7 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
     }
   }
   __syncthreads();
+  mark(tr);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int grp = lane >> 4, sub = lane & 15;
@@ -1144,15 +1172,17 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
 // Units wg, wg + n_wg, ... of this workgroup (one unit unless the grid is
 // smaller than the number of KV heads, in which case there is one split per
 // head and no merge); `pre` holds the first unit's first cache rows.
-template <int G, bool kPre, bool kMerge>
+template <int G, bool kMerge>
 __device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int pos, int wg, Lds s,
-                                           KVPre pre, const Ctl& c, Tracer& tr) {
+                                           const Ctl& c, Tracer& tr) {
   const int units = p.nkv * p.splits;
   if (wg >= units) {
     mark(tr);
+    mark(tr);
     return true;
   }
-  if (!attn_unit<G, kPre, kMerge>(p, step, l, pos, attn_unit_of(p, pos, wg), s.h, pre, c, tr))
+  const KVPre pre = prefetch_attn(p, l, pos, wg);
+  if (!attn_unit<G, true, kMerge>(p, step, l, pos, attn_unit_of(p, pos, wg), s.h, pre, c, tr))
     return false;
   __syncthreads();
   for (int u = wg + p.n_wg; u < units; u += p.n_wg) {
@@ -1180,15 +1210,13 @@ __device__ __forceinline__ GemvWork o_work(const Params& p, int wg) {
   return gemv_work(p.d, p.H * p.hd, p.n_wg, wg, false);
 }
 __device__ __forceinline__ RowAddr o_addr(const Params& p, int l) {
-  return RowAddr{mat_rsrc(p.layers[l].wo, p.d, p.H * p.hd), p.H * p.hd};
+  return RowAddr{mat_rsrc(layer(p, l).wo, p.d, p.H * p.hd), p.H * p.hd};
 }
-__device__ __forceinline__ WPre prefetch_o(const Params& p, int l, int wg) {
-  return gemv_prefetch(o_work(p, wg), o_addr(p, l));
-}
-template <bool kPre>
 __device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, const __half* emb_row,
-                                            int wg, Lds s, WPre pre, const Ctl& c, Tracer& tr) {
+                                            int wg, Lds s, const Ctl& c, Tracer& tr) {
   const GemvWork g = o_work(p, wg);
+  const RowAddr addr = o_addr(p, l);
+  const WPre pre = gemv_prefetch(g, addr);
   const int qd = p.H * p.hd;
   const int nown = g.r1 - g.r0;
   if (l == 0) {
@@ -1199,8 +1227,9 @@ __device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, co
                           l == 0 ? 0u : ll_flag(p, step, l - 1, kSlotXDown)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXO);
-  gemv_run<kPre>(g, o_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; i < n; i += kThreads) {
       const int r = b0 + i;
       ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
@@ -1217,28 +1246,28 @@ __device__ __forceinline__ GemvWork gu_work(const Params& p, int wg) {
   return g;
 }
 __device__ __forceinline__ PairAddr gu_addr(const Params& p, int l) {
-  const LayerPtrs& w = p.layers[l];
-  return PairAddr{w.w_gate, w.w_up, p.F, p.d};
+  const LayerPtrs w = layer(p, l);
+  return PairAddr{uniform_addr(w.w_gate), uniform_addr(w.w_up), p.F, p.d};
 }
-__device__ __forceinline__ WPre prefetch_gateup(const Params& p, int l, int wg) {
-  return gemv_prefetch(gu_work(p, wg), gu_addr(p, l));
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+__device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, int wg, Lds s,
                                              const Ctl& c, Tracer& tr) {
   const GemvWork g = gu_work(p, wg);
+  const PairAddr addr = gu_addr(p, l);
+  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
+    mark(tr);
     mark(tr);
     return true;
   }
-  const __half* gain = p.layers[l].ffn_norm;
+  const __half* gain = layer(p, l).ffn_norm;
   const GainPre G = gain_prefetch(gain, p.d);
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
   rmsnorm_lds(p, gain, G, s.h, s.red);
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotU);
-  gemv_run<kPre>(g, gu_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; 2 * i < n; i += kThreads)
       ll_put(p, p.off_u + (b0 >> 1) + i, silu(sums[2 * i]) * sums[2 * i + 1], f);
   });
@@ -1250,22 +1279,21 @@ __device__ __forceinline__ GemvWork down_work(const Params& p, int wg) {
   return gemv_work(p.d, p.F, p.n_wg, wg, false);
 }
 __device__ __forceinline__ RowAddr down_addr(const Params& p, int l) {
-  return RowAddr{mat_rsrc(p.layers[l].w_down, p.d, p.F), p.F};
+  return RowAddr{mat_rsrc(layer(p, l).w_down, p.d, p.F), p.F};
 }
-__device__ __forceinline__ WPre prefetch_down(const Params& p, int l, int wg) {
-  return gemv_prefetch(down_work(p, wg), down_addr(p, l));
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+__device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int wg, Lds s,
                                            const Ctl& c, Tracer& tr) {
   const GemvWork g = down_work(p, wg);
+  const RowAddr addr = down_addr(p, l);
+  const WPre pre = gemv_prefetch(g, addr);
   const int nown = g.r1 - g.r0;
   const LLRange rg[2] = {{p.off_u, p.F, s.h, ll_flag(p, step, l, kSlotU)},
                          {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXDown);
-  gemv_run<kPre>(g, down_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; i < n; i += kThreads) {
       const int r = b0 + i;
       ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
@@ -1283,27 +1311,27 @@ __device__ __forceinline__ GemvWork router_work(const Params& p, int wg) {
   return gemv_work(p.E, p.d, p.n_wg, wg, false);
 }
 __device__ __forceinline__ RowAddr router_addr(const Params& p, int l) {
-  return RowAddr{mat_rsrc(p.layers[l].router, p.E, p.d), p.d};
+  return RowAddr{mat_rsrc(layer(p, l).router, p.E, p.d), p.d};
 }
-__device__ __forceinline__ WPre prefetch_router(const Params& p, int l, int wg) {
-  return gemv_prefetch(router_work(p, wg), router_addr(p, l));
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_router(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+__device__ __forceinline__ bool stage_router(const Params& p, int step, int l, int wg, Lds s,
                                              const Ctl& c, Tracer& tr) {
   const GemvWork g = router_work(p, wg);
+  const RowAddr addr = router_addr(p, l);
+  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
+    mark(tr);
     mark(tr);
     return true;
   }
-  const __half* gain = p.layers[l].ffn_norm;
+  const __half* gain = layer(p, l).ffn_norm;
   const GainPre G = gain_prefetch(gain, p.d);
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
   rmsnorm_lds(p, gain, G, s.h, s.red);
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotRouter);
-  gemv_run<kPre>(g, router_addr(p, l), s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_router + b0 + i, sums[i], f);
   });
   return true;
@@ -1348,7 +1376,7 @@ __device__ __forceinline__ GemvWork moe_gu_work(const Params& p, int wg) {
 }
 __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int l, int wg, Lds s,
                                                  const Ctl& c, Tracer& tr) {
-  const LayerPtrs& w = p.layers[l];
+  const LayerPtrs w = layer(p, l);
   int* ids = moe_ids(s);
   float* wts = moe_wts(s);
   const GemvWork g = moe_gu_work(p, wg);
@@ -1362,10 +1390,14 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
   moe_routing(p, ids, wts, s.sums);
   if (p.mode == kDecode && wg == 0 && threadIdx.x < p.topk)
     p.expert_log[((size_t)step * p.L + l) * p.topk + threadIdx.x] = ids[threadIdx.x];
-  if (!rows) return true;
+  if (!rows) {
+    mark(tr);
+    return true;
+  }
   rmsnorm_lds(p, gain, G, s.h, s.red);
+  mark(tr);
   const int Fe = p.Fe, ne = p.E + p.nshared;
-  const MoePairAddr addr{w.e_gate, w.e_up, ids, ne, Fe, p.d};
+  const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
   const unsigned f = ll_flag(p, step, l, kSlotU);
   gemv_run<false>(g, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; 2 * i < n; i += kThreads) {
@@ -1382,17 +1414,16 @@ __device__ __forceinline__ GemvWork moe_down_work(const Params& p, int wg) {
   return gemv_work(p.d, (p.topk + p.nshared) * p.Fe, p.n_wg, wg, false);
 }
 __device__ __forceinline__ MoeDownAddr moe_down_addr(const Params& p, int l, Lds s) {
-  return MoeDownAddr{mat_rsrc(p.layers[l].e_down, (p.E + p.nshared) * p.d, p.Fe), moe_ids(s), p.Fe,
+  return MoeDownAddr{mat_rsrc(layer(p, l).e_down, (p.E + p.nshared) * p.d, p.Fe), moe_ids(s), p.Fe,
                      p.d, p.Fe >> 3};
 }
-// Expert ids are already in LDS (from the gate/up stage of this layer).
-__device__ __forceinline__ WPre prefetch_moe_down(const Params& p, int l, int wg, Lds s) {
-  return gemv_prefetch(moe_down_work(p, wg), moe_down_addr(p, l, s));
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l, int wg, Lds s, WPre pre,
+// With have_routing the expert ids are already in LDS (from this layer's
+// gate/up stage), so the first expert rows can be issued before the wait.
+__device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l, int wg, Lds s,
                                                bool have_routing, const Ctl& c, Tracer& tr) {
   const GemvWork g = moe_down_work(p, wg);
+  WPre pre = {};
+  if (have_routing) pre = gemv_prefetch(g, moe_down_addr(p, l, s));
   const int nown = g.r1 - g.r0;
   const int A = p.topk + p.nshared;
   const LLRange rg[3] = {{p.off_u, A * p.Fe, s.h, ll_flag(p, step, l, kSlotU)},
@@ -1400,9 +1431,16 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
                          {p.off_router, have_routing ? 0 : p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
-  if (!have_routing) moe_routing(p, moe_ids(s), moe_wts(s), s.sums);
+  if (!have_routing) {
+    moe_routing(p, moe_ids(s), moe_wts(s), s.sums);
+    int t0, t1;
+    wave_tasks(g, g.r0, t0, t1);
+    pre.a = wload(moe_down_addr(p, l, s), g, g.r0, t0, t1);
+    pre.b = wload(moe_down_addr(p, l, s), g, g.r0, t0 + kBatch, t1);
+  }
+  mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXDown);
-  gemv_run<kPre>(g, moe_down_addr(p, l, s), s.h, s.part, s.sums, pre,
+  gemv_run<true>(g, moe_down_addr(p, l, s), s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
                    for (int i = threadIdx.x; i < n; i += kThreads) {
                      const int r = b0 + i;
@@ -1420,14 +1458,13 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
 __device__ __forceinline__ GemvWork lm_work(const Params& p, int wg) {
   return gemv_work(p.Vout, p.d, p.n_wg, wg, false);
 }
-__device__ __forceinline__ WPre prefetch_lmhead(const Params& p, int wg) {
-  return gemv_prefetch(lm_work(p, wg), RowAddr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d});
-}
-template <bool kPre>
-__device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, Lds s, WPre pre,
-                                             const Ctl& c, Tracer& tr) {
+__device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, Lds s, const Ctl& c,
+                                             Tracer& tr) {
   const GemvWork g = lm_work(p, wg);
+  const RowAddr addr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d};
+  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
+    mark(tr);
     mark(tr);
     return true;
   }
@@ -1436,9 +1473,10 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
   rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
+  mark(tr);
   float* logits = p.out_logits ? p.out_logits + (size_t)step * p.Vout : nullptr;
   unsigned long long best = 0ull;
-  gemv_run<kPre>(g, RowAddr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d}, s.h, s.part, s.sums, pre,
+  gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
                    for (int i = threadIdx.x; i < n; i += kThreads) {
                      const float v = sums[i];
@@ -1507,66 +1545,60 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
     trace = (decode && p.trace != nullptr) ? p.trace + (size_t)wg * kTraceEvents : nullptr;
     trace_step = p.trace_step;
   }
-  WPre wpre = prefetch_qkv(fresh(pp), 0, wg);
+  // Input token of step `prev + 1`, once the grid barrier that closed step
+  // `prev` has been passed: the argmax of its logits (decode) or the next
+  // prompt token (prefill).
+  auto resolve = [&](int prev) -> int {
+    const Params& p = fresh(pp);
+    if (!decode) return p.prompt[prev + 1];
+    const int t = argmax_index(ld_c64(p.amax + (prev & 1)), p.Vout);
+    if (wg == 0 && threadIdx.x == 0) {
+      p.out_tokens[prev] = t;
+      st_c64(p.amax + ((prev + 1) & 1), 0ull);
+    }
+    return t;
+  };
   for (int step = 0; step < n_steps; ++step) {
     const int pos = pos0 + step;
     tr.tr = (step == trace_step) ? trace : nullptr;
     tr.ev = 0;
     mark(tr);
     for (int l = 0; l < L; ++l) {
+      if (!stage_qkv(fresh(pp), step, l, wg, s, c, tr, gs, l == 0 && step > 0, tok,
+                     [&]() { return resolve(step - 1); }))
+        return;
+      mark(tr);
+      if (!stage_attn<G, true>(fresh(pp), step, l, pos, wg, s, c, tr)) return;
+      mark(tr);
       {
         const Params& p = fresh(pp);
-        if (!stage_qkv<true>(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre, c, tr)) return;
-      }
-      mark(tr);
-      const KVPre kvpre = prefetch_attn(fresh(pp), l, pos, wg);
-      if (!stage_attn<G, true, true>(fresh(pp), step, l, pos, wg, s, kvpre, c, tr)) return;
-      mark(tr);
-      wpre = prefetch_o(fresh(pp), l, wg);
-      {
-        const Params& p = fresh(pp);
-        if (!stage_oproj<true>(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, wpre, c, tr)) return;
+        if (!stage_oproj(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, c, tr)) return;
       }
       mark(tr);
       if (!moe) {
-        wpre = prefetch_gateup(fresh(pp), l, wg);
-        if (!stage_gateup<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
+        if (!stage_gateup(fresh(pp), step, l, wg, s, c, tr)) return;
         mark(tr);
-        wpre = prefetch_down(fresh(pp), l, wg);
-        if (!stage_down<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
+        if (!stage_down(fresh(pp), step, l, wg, s, c, tr)) return;
       } else {
-        wpre = prefetch_router(fresh(pp), l, wg);
-        if (!stage_router<true>(fresh(pp), step, l, wg, s, wpre, c, tr)) return;
+        if (!stage_router(fresh(pp), step, l, wg, s, c, tr)) return;
         mark(tr);
         if (!stage_moe_gateup(fresh(pp), step, l, wg, s, c, tr)) return;
         mark(tr);
-        wpre = prefetch_moe_down(fresh(pp), l, wg, s);
-        if (!stage_moe_down<true>(fresh(pp), step, l, wg, s, wpre, true, c, tr)) return;
+        if (!stage_moe_down(fresh(pp), step, l, wg, s, true, c, tr)) return;
       }
       mark(tr);
-      if (l + 1 < L) wpre = prefetch_qkv(fresh(pp), l + 1, wg);
     }
     if (decode) {
-      wpre = prefetch_lmhead(fresh(pp), wg);
-      if (!stage_lmhead<true>(fresh(pp), step, wg, s, wpre, c, tr)) return;
+      if (!stage_lmhead(fresh(pp), step, wg, s, c, tr)) return;
       mark(tr);
-      grid_arrive(gs);
-      wpre = prefetch_qkv(fresh(pp), 0, wg);
-      if (!grid_wait(gs, &flag)) return;
-      mark(tr);
-      const Params& p = fresh(pp);
-      tok = argmax_index(ld_c64(p.amax + (step & 1)), p.Vout);
-      if (wg == 0 && threadIdx.x == 0) {
-        p.out_tokens[step] = tok;
-        st_c64(p.amax + ((step + 1) & 1), 0ull);
-      }
-    } else {
-      // the next prefill step's first attention reads this step's KV rows
-      grid_arrive(gs);
-      wpre = prefetch_qkv(fresh(pp), 0, wg);
-      if (!grid_wait(gs, &flag)) return;
-      tok = fresh(pp).prompt[step + 1];
     }
+    // closes the step: the argmax is complete (decode); this step's KV rows,
+    // read by the next step's attention, are written (prefill)
+    grid_arrive(gs);
+  }
+  if (n_steps > 0) {
+    if (!grid_wait(gs, &flag)) return;
+    tok = resolve(n_steps - 1);
   }
   if (wg == 0 && threadIdx.x == 0) {
     const Params& p = fresh(pp);
@@ -1590,13 +1622,15 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage,
   const int tok = (p.mode == kPrefill) ? p.prompt[step] : p.state[0];
   const __half* emb = p.tok_emb + (size_t)tok * p.d;
   Tracer none{nullptr, 0};
+  GridSync no_sync = make_sync(p.bar, p.err, (unsigned)p.n_wg, p.timeout_ticks, p.spin_limit);
+  int t = tok;
   switch (stage) {
-    case kSQkv: (void)stage_qkv<false>(p, step, l, emb, wg, s, WPre{}, c, none); break;
+    case kSQkv: (void)stage_qkv(p, step, l, wg, s, c, none, no_sync, false, t, [&]() { return tok; }); break;
     case kSAttn:
       switch (p.H / p.nkv) {
-        case 1: (void)stage_attn<1, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
-        case 2: (void)stage_attn<2, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
-        default: (void)stage_attn<4, false, false>(p, step, l, pos, wg, s, KVPre{}, c, none); break;
+        case 1: (void)stage_attn<1, false>(p, step, l, pos, wg, s, c, none); break;
+        case 2: (void)stage_attn<2, false>(p, step, l, pos, wg, s, c, none); break;
+        default: (void)stage_attn<4, false>(p, step, l, pos, wg, s, c, none); break;
       }
       break;
     case kSMerge:
@@ -1606,13 +1640,13 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage,
         default: (void)stage_merge<4>(p, step, l, wg, s, c); break;
       }
       break;
-    case kSO: (void)stage_oproj<false>(p, step, l, emb, wg, s, WPre{}, c, none); break;
-    case kSGateUp: (void)stage_gateup<false>(p, step, l, wg, s, WPre{}, c, none); break;
-    case kSDown: (void)stage_down<false>(p, step, l, wg, s, WPre{}, c, none); break;
-    case kSRouter: (void)stage_router<false>(p, step, l, wg, s, WPre{}, c, none); break;
+    case kSO: (void)stage_oproj(p, step, l, emb, wg, s, c, none); break;
+    case kSGateUp: (void)stage_gateup(p, step, l, wg, s, c, none); break;
+    case kSDown: (void)stage_down(p, step, l, wg, s, c, none); break;
+    case kSRouter: (void)stage_router(p, step, l, wg, s, c, none); break;
     case kSMoeGateUp: (void)stage_moe_gateup(p, step, l, wg, s, c, none); break;
-    case kSMoeDown: (void)stage_moe_down<false>(p, step, l, wg, s, WPre{}, false, c, none); break;
-    case kSLm: (void)stage_lmhead<false>(p, step, wg, s, WPre{}, c, none); break;
+    case kSMoeDown: (void)stage_moe_down(p, step, l, wg, s, false, c, none); break;
+    case kSLm: (void)stage_lmhead(p, step, wg, s, c, none); break;
   }
 }
 

@@ -476,9 +476,10 @@ int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits)
   if (p.trace) {
     const int per_layer = h->cfg.n_experts ? 6 : 5;
     // step start; for every stage (per_layer per layer, then lm_head) the
-    // moment its inputs were complete and the moment it finished; the
-    // argmax barrier's release
-    h->trace_events = std::min(kie::kTraceEvents, 1 + 2 * (h->cfg.n_layers * per_layer + 1) + 1);
+    // moment its inputs were complete, the moment its main loop started and
+    // the moment it finished (the previous step's argmax barrier is waited
+    // for inside the first stage)
+    h->trace_events = std::min(kie::kTraceEvents, 1 + 3 * (h->cfg.n_layers * per_layer + 1));
   }
   return KIE_OK;
 }
