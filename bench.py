@@ -12,6 +12,7 @@ the CPU oracle timed on the host's cores on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,7 +23,35 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("persistent_decode_monokernel_amd/csrc/kie_kernels.hip",
+                  "persistent_decode_monokernel_amd/csrc/kie_params.h",
+                  "persistent_decode_monokernel_amd/csrc/kie_runtime.hip")
+# HBM bytes of one timed decode launch, from two rocprofv3 counter passes
+# (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for the
+# streaming probe kernel of known size; the summary with the commands is
+# profiles/mono_kernel_2b_decode512.md.  A figure is reported only while the
+# kernel sources still hash to the digest it was measured on.
+MEASURED_TRAFFIC = [
+    {"sources_sha256": "61b63638ec2128f75ed84aec685fcc33477e62d5c745a85f7dcdc41657b0bdc5",
+     "config": "2b", "pos0": 511, "steps": 512, "bytes": 2242372151622},
+]
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs ~8 TB/s peak, ~2.2B fp16"
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cfg, pos0: int, steps: int):
+    digest = source_digest()
+    for m in MEASURED_TRAFFIC:
+        if (m["sources_sha256"], m["config"], m["pos0"], m["steps"]) == (digest, cfg.name, pos0, steps):
+            return m["bytes"]
+    return None
 
 
 def weight_bytes_per_token(c) -> int:
@@ -151,8 +180,10 @@ def main(argv=None):
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming probes")
     ap.add_argument("--trace", action="store_true",
                     help="also run one traced decode and add a per-stage breakdown to detail")
-    ap.add_argument("--plain-launch", action="store_true",
-                    help="launch the persistent kernel with an ordinary dispatch")
+    ap.add_argument("--cooperative", action="store_true",
+                    help="launch the persistent kernel as a cooperative dispatch (the default is "
+                         "an ordinary dispatch, which profilers can trace; residency of every "
+                         "workgroup is checked at engine creation either way)")
     ap.add_argument("--probe-only", action="store_true",
                     help="run only the HBM read/copy probes (counter calibration)")
     args = ap.parse_args(argv)
@@ -183,7 +214,7 @@ def main(argv=None):
     prompt = make_prompt(cfg, seed=0)
     stream = torch.cuda.current_stream()
 
-    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph, plain_launch=args.plain_launch)
+    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph, plain_launch=not args.cooperative)
     eng.prefill(prompt)
     if args.warmup:
         eng.decode(args.warmup, logits=False)
@@ -210,7 +241,7 @@ def main(argv=None):
     eng.close()
     trace = None
     if args.trace and not args.graph:
-        te = kie.Engine(cfg, W, max_seq=max_seq, trace=True, plain_launch=args.plain_launch)
+        te = kie.Engine(cfg, W, max_seq=max_seq, trace=True, plain_launch=not args.cooperative)
         te.prefill(prompt)
         te.decode_into(min(K, 8), toks, None)
         trace = trace_summary(cfg, te.read_trace())
@@ -240,7 +271,8 @@ def main(argv=None):
                    "global_batch": 1, "seq_len": P + K,
                    "mode": "staged-hipgraph" if args.graph else "persistent"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(cfg, P - 1, K)},
         "detail": {"kernel": "kie::mono_kernel" if not args.graph else "kie::stage_kernel",
                    "bytes_per_launch": nbytes, "bytes_per_token": nbytes / K,
                    "kernel_ms": kms, "call_ms": ms, "reps_call_ms": times,
