@@ -175,9 +175,11 @@ int kie_last_elapsed_ms(const kie_handle *h, float *ms);
 int kie_debug_read_kv(const kie_handle *h, int32_t layer, int32_t pos0, int32_t pos1,
                       void *k_host, void *v_host);
 
-/* MoE only: routed expert ids chosen by the last kie_decode call, host int32
- * [n_steps][n_layers][top_k] in rank order (largest probability first). */
-int kie_debug_expert_ids(const kie_handle *h, int32_t *ids_host, int32_t n_steps);
+/* MoE only: the routed expert ids chosen at positions [pos0, pos1) by
+ * prefill or decode, host int32 [pos1-pos0][n_layers][top_k] in rank order
+ * (largest probability first; ties to the lower id).  pos1 may not exceed
+ * the current position (kie_get_position); INVALID_ARG otherwise. */
+int kie_debug_expert_ids(const kie_handle *h, int32_t pos0, int32_t pos1, int32_t *ids_host);
 
 /* y = W x with the decode kernel's GEMV stage code: W device fp16 [rows][cols]
  * row-major (cols a multiple of 8), x device fp32 [cols], y device fp32

@@ -117,15 +117,18 @@ def moe_route(r: np.ndarray, top_k: int):
 
 
 def moe_ffn(h: np.ndarray, router: np.ndarray, expert, n_experts: int, top_k: int,
-            n_shared: int) -> tuple:
+            n_shared: int, router_log: Optional[list] = None) -> tuple:
     """Mixture-of-experts FFN for one token.
 
     y = sum over shared experts s of SwiGLU_s(h) + sum over the selected routed
     experts e of pi_e * SwiGLU_e(h).  ``expert(e)`` returns the widened
     (gate, up, down) of expert e; ids n_experts.. are the shared experts.
     Only the experts used are touched (active-parameter streaming).
-    Returns (y, selected ids)."""
+    Returns (y, selected ids); the router logits are appended to
+    ``router_log`` when one is given (for judging near-ties in routing)."""
     r = router @ h
+    if router_log is not None:
+        router_log.append(r)
     pi, sel = moe_route(r, top_k)
     y = np.zeros_like(h)
     for s in range(n_shared):
@@ -166,6 +169,8 @@ class Oracle:
         self._cache_bytes = 0
         self._cache_limit = cache_bytes
         self.expert_log = []        # per decode step: [layer] -> selected ids
+        self.router_log = []        # per decode step: [layer] -> router logits
+        self.route = {}             # position -> (ids [L][top_k], router logits [L][E])
         self.reset()
 
     # -- weights ----------------------------------------------------------
@@ -204,6 +209,8 @@ class Oracle:
         self.pos = 0
         self.pending: Optional[int] = None
         self.expert_log = []
+        self.router_log = []
+        self.route = {}
 
     def _store_kv(self, l, p, k, v):
         if self.kv_fp16:
@@ -212,12 +219,12 @@ class Oracle:
         self.K[l][:, p] = k
         self.V[l][:, p] = v
 
-    def _ffn(self, l: int, h: np.ndarray):
+    def _ffn(self, l: int, h: np.ndarray, router_log: Optional[list] = None):
         c = self.cfg
         if not c.is_moe:
             return swiglu(h, self.lw(l, "w_gate"), self.lw(l, "w_up"), self.lw(l, "w_down")), None
         return moe_ffn(h, self.lw(l, "router"), lambda e: self.expert(l, e),
-                       c.n_experts, c.top_k, c.n_shared_experts)
+                       c.n_experts, c.top_k, c.n_shared_experts, router_log)
 
     # -- one token ----------------------------------------------------------
     def step(self, tok: int) -> np.ndarray:
@@ -232,7 +239,7 @@ class Oracle:
         eps = c.rms_eps
         x = self.w["tok_emb"][tok].astype(self.dt)
         cos, sin = rope_cos_sin(p, hd, c.rope_base, self.dt)
-        experts = []
+        experts, router = [], []
         for l in range(c.n_layers):
             h = rmsnorm(x, self.w["layers"][l]["attn_norm"], eps)
             q = (self.lw(l, "wq") @ h).reshape(H, hd)
@@ -247,13 +254,15 @@ class Oracle:
                 o[i] = attend(q[i], self.K[l][g, :p + 1], self.V[l][g, :p + 1])
             x = x + self.lw(l, "wo") @ o.reshape(-1)
             h = rmsnorm(x, self.w["layers"][l]["ffn_norm"], eps)
-            y, sel = self._ffn(l, h)
+            y, sel = self._ffn(l, h, router)
             if sel is not None:
                 experts.append(np.asarray(sel, np.int32))
             x = x + y
         self.pos = p + 1
         if experts:
             self.expert_log.append(np.stack(experts))
+            self.router_log.append(np.stack(router))
+            self.route[p] = (self.expert_log[-1], self.router_log[-1])
         return self.gw("lm_head") @ rmsnorm(x, self.w["final_norm"], eps)
 
     # -- prompt ---------------------------------------------------------------
@@ -275,6 +284,7 @@ class Oracle:
                 for tok in t[:-1]:
                     self.step(int(tok))
             self.expert_log = []
+            self.router_log = []
         self.pos = P - 1
         self.pending = int(t[-1])
 
@@ -306,10 +316,18 @@ class Oracle:
             X = X + O.reshape(n, H * hd) @ self.lw(l, "wo").T
             Hn = rmsnorm(X, self.w["layers"][l]["ffn_norm"], eps)
             if c.is_moe:
-                Y = np.stack([self._ffn(l, Hn[p])[0] for p in range(n)])
+                Y = np.empty_like(X)
+                for p in range(n):
+                    r = []
+                    Y[p], sel = self._ffn(l, Hn[p], r)
+                    ids, rl = self.route.get(p, ([], []))
+                    self.route[p] = (list(ids) + [np.asarray(sel, np.int32)], list(rl) + r)
             else:
                 Y = swiglu(Hn, self.lw(l, "w_gate"), self.lw(l, "w_up"), self.lw(l, "w_down"))
             X = X + Y
+        for p in list(self.route):
+            ids, rl = self.route[p]
+            self.route[p] = (np.stack(ids), np.stack(rl))
 
     # -- generation -------------------------------------------------------------
     def decode(self, n: int, force: Optional[Sequence[int]] = None, keep_logits: bool = True):

@@ -78,7 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_last_error": (ctypes.c_char_p, []),
         "kie_last_elapsed_ms": (ctypes.c_int, [VP, P(ctypes.c_float)]),
         "kie_debug_read_kv": (ctypes.c_int, [VP, I32, I32, I32, VP, VP]),
-        "kie_debug_expert_ids": (ctypes.c_int, [VP, P(I32), I32]),
+        "kie_debug_expert_ids": (ctypes.c_int, [VP, I32, I32, P(I32)]),
         "kie_debug_gemv": (ctypes.c_int, [VP, VP, VP, I32, I32, I32, VP]),
         "kie_debug_barrier": (ctypes.c_int, [I32, I32, I32, P(I32), P(ctypes.c_float), VP]),
         "kie_debug_read_trace": (ctypes.c_int, [VP, P(ctypes.c_uint64), I32, P(I32), P(I32)]),

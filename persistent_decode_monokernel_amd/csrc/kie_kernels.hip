@@ -1388,8 +1388,8 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
   moe_routing(p, ids, wts, s.sums);
-  if (p.mode == kDecode && wg == 0 && threadIdx.x < p.topk)
-    p.expert_log[((size_t)step * p.L + l) * p.topk + threadIdx.x] = ids[threadIdx.x];
+  if (wg == 0 && threadIdx.x < p.topk)
+    p.expert_log[((size_t)(p.pos0 + step) * p.L + l) * p.topk + threadIdx.x] = ids[threadIdx.x];
   if (!rows) {
     mark(tr);
     return true;

@@ -61,7 +61,7 @@ struct Params {
   unsigned long long* amax;     // [2] packed (logit, index) argmax slots
   int* err;                     // device error word (0 = ok)
   int* state;                   // [0] pending token, [1] graph-mode step counter
-  int* expert_log;              // [cap][L][topk] MoE routing record (decode)
+  int* expert_log;              // [cap][L][topk] MoE routing record, by position
   // ---- per call
   int mode;                     // kPrefill / kDecode
   int n_steps;

@@ -532,17 +532,18 @@ int kie_debug_read_kv(const kie_handle* h, int32_t layer, int32_t pos0, int32_t 
   return KIE_OK;
 }
 
-int kie_debug_expert_ids(const kie_handle* h, int32_t* ids_host, int32_t n_steps) {
+int kie_debug_expert_ids(const kie_handle* h, int32_t pos0, int32_t pos1, int32_t* ids_host) {
   g_err.clear();
   if (!h || !ids_host) return fail(KIE_ERR_INVALID_ARG, "handle or ids is NULL");
   const kie_config& c = h->cfg;
   if (c.n_experts == 0) return fail(KIE_ERR_INVALID_ARG, "not a MoE model");
-  if (n_steps < 0 || n_steps > h->last_decode_steps)
-    return fail(KIE_ERR_INVALID_ARG, "n_steps exceeds the last decode call");
+  if (pos0 < 0 || pos1 < pos0 || pos1 > h->pos)
+    return fail(KIE_ERR_INVALID_ARG, "position range is not inside the processed positions");
   KIE_HIP(hipStreamSynchronize(h->stream));
-  if (n_steps)
-    KIE_HIP(hipMemcpy(ids_host, h->base.expert_log,
-                      sizeof(int) * (size_t)n_steps * c.n_layers * c.top_k, hipMemcpyDeviceToHost));
+  const size_t row = (size_t)c.n_layers * c.top_k;
+  if (pos1 > pos0)
+    KIE_HIP(hipMemcpy(ids_host, h->base.expert_log + (size_t)pos0 * row,
+                      sizeof(int) * (size_t)(pos1 - pos0) * row, hipMemcpyDeviceToHost));
   return KIE_OK;
 }
 

@@ -116,11 +116,13 @@ class Engine:
               "kie_debug_read_kv")
         return k, v
 
-    def expert_ids(self, n_steps: int) -> np.ndarray:
+    def expert_ids(self, pos0: int, pos1: int) -> np.ndarray:
+        """MoE routing at positions [pos0, pos1): int32 [pos1-pos0][n_layers][top_k]."""
         m = self.model
-        ids = np.empty((n_steps, m.n_layers, m.top_k), np.int32)
-        check(self.lib.kie_debug_expert_ids(self.h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                            n_steps), "kie_debug_expert_ids")
+        ids = np.empty((max(0, pos1 - pos0), m.n_layers, m.top_k), np.int32)
+        check(self.lib.kie_debug_expert_ids(self.h, pos0, pos1,
+                                            ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+              "kie_debug_expert_ids")
         return ids
 
     def read_trace(self) -> np.ndarray:

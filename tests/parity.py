@@ -78,3 +78,45 @@ def kv_rows_close(k_gpu_f16: np.ndarray, k_or: np.ndarray, what: str, rel: float
     bad = err > rel * scale
     assert not bad.any(), (f"{what}: {int(bad.sum())} rows off, worst relative "
                            f"{float(np.max(err / np.maximum(scale, 1e-30))):.3e}")
+
+
+ROUTE_TIE = 1e-3
+
+
+def compare_routing(ids_gpu: np.ndarray, ids_or: np.ndarray, router_or, top_k: int,
+                    where: dict = None):
+    """Routed expert ids per (position, layer), in rank order, against the oracle's.
+
+    Where the ids differ, the GPU's choice must still be a top-k of the
+    oracle's router logits r to within ``ROUTE_TIE``: its rank order is
+    non-increasing in r up to the tolerance, and every chosen expert's logit
+    is at least every unchosen expert's minus the tolerance (several
+    routings are correct when logits are within fp32 noise of each other).
+    Returns the sorted list of positions whose expert set differs (their
+    outputs are not held to the bar).  Once a layer's expert set differs,
+    the layers above it at that position see a different input, so they
+    are not compared.  ``where`` (a dict) receives position -> that layer."""
+    ids_gpu = np.asarray(ids_gpu)
+    ids_or = np.asarray(ids_or)
+    assert ids_gpu.shape == ids_or.shape, (ids_gpu.shape, ids_or.shape)
+    tied = set()
+    for i in range(ids_gpu.shape[0]):
+        for l in range(ids_gpu.shape[1]):
+            if i in tied:
+                break
+            g = ids_gpu[i, l]
+            if np.array_equal(g, ids_or[i, l]):
+                continue
+            r = np.asarray(router_or[i][l], np.float64)
+            assert len(set(g.tolist())) == top_k and np.all((g >= 0) & (g < len(r))), g
+            rest = np.setdiff1d(np.arange(len(r)), g)
+            order_ok = bool(np.all(r[g[:-1]] >= r[g[1:]] - ROUTE_TIE))
+            set_ok = len(rest) == 0 or float(r[g].min()) >= float(r[rest].max()) - ROUTE_TIE
+            assert order_ok and set_ok, (
+                f"position {i} layer {l}: gpu experts {g.tolist()} != oracle "
+                f"{ids_or[i, l].tolist()} (logits of gpu choice {np.round(r[g], 5).tolist()})")
+            if not np.array_equal(np.sort(g), np.sort(ids_or[i, l])):
+                tied.add(i)
+                if where is not None:
+                    where[i] = l
+    return sorted(tied)

@@ -10,7 +10,7 @@ import pytest
 
 from kie_synth import get_config, make_prompt, make_weights, weights_to_numpy
 from oracle import Oracle
-from tests.parity import compare_steps, kv_close, kv_rows_close
+from tests.parity import compare_routing, compare_steps, kv_close, kv_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -89,23 +89,31 @@ def _run_gpu(torch, kie, cfg, W, prompt, n, **kw):
 
 
 def _oracle_replay(cfg, Wn, prompt, toks):
-    o = Oracle(cfg, Wn)
+    # Expert routing is an integer decision taken from floating point: for a
+    # MoE model the oracle stores its KV rows in the kernel's cache precision
+    # (fp16) so that both sides route from the same rounded cache.
+    o = Oracle(cfg, Wn, kv_fp16=cfg.is_moe)
     o.prefill(prompt)
     _, z = o.decode(len(toks), force=toks)
     return o, z
 
 
-def _check_kv(eng, o, layers, spans):
+def _check_kv(eng, o, layers, spans, exclude=()):
     """Layer 0 sees identical inputs on both sides: half an fp16 ulp.  Every
-    listed layer: each row within 1e-2 of its largest magnitude."""
+    listed layer: each row within 1e-2 of its largest magnitude.  Positions
+    in ``exclude`` (an accepted MoE routing near-tie) are skipped above
+    layer 0, whose rows do not depend on routing."""
     for l in layers:
         for p0, p1 in spans:
             k, v = eng.read_kv(l, p0, p1)
             if l == 0:
-                kv_close(k, o.K[0][:, p0:p1], f"K layer 0 [{p0},{p1})")
-                kv_close(v, o.V[0][:, p0:p1], f"V layer 0 [{p0},{p1})")
-            kv_rows_close(k, o.K[l][:, p0:p1], f"K layer {l} [{p0},{p1})")
-            kv_rows_close(v, o.V[l][:, p0:p1], f"V layer {l} [{p0},{p1})")
+                # against an fp16-rounded oracle cache both sides round: 1 ulp
+                u = 1.0 if o.kv_fp16 else 0.5
+                kv_close(k, o.K[0][:, p0:p1], f"K layer 0 [{p0},{p1})", ulps=u)
+                kv_close(v, o.V[0][:, p0:p1], f"V layer 0 [{p0},{p1})", ulps=u)
+            keep = [j - p0 for j in range(p0, p1) if j not in exclude]
+            kv_rows_close(k[:, keep], o.K[l][:, p0:p1][:, keep], f"K layer {l} [{p0},{p1})")
+            kv_rows_close(v[:, keep], o.V[l][:, p0:p1][:, keep], f"V layer {l} [{p0},{p1})")
 
 
 @pytest.mark.parametrize("mode", ["persistent", "graph", "persistent_7wg", "graph_5wg", "persistent_3wg"])
@@ -221,4 +229,116 @@ def test_2b_full_size_parity_sampled(torch, kie):
     P = len(prompt)
     _check_kv(eng, o, (0, 12, 24),
               [(0, 1), (255, 256), (P - 2, P - 1), (P - 1 + n - 1, P - 1 + n)])
+    eng.close()
+
+
+# ------------------------------------------- the other workload shapes
+# Reduced depth keeps the oracle's replay to seconds; widths, head layout,
+# vocabulary split and expert counts are those of the full workloads.
+VARIANTS = {
+    # one tensor-parallel-8 share run standalone: 3 heads x 128, FFN 864,
+    # 32768-row embedding but a 4096-row lm_head
+    "tp8share_3l": dict(name="tp8share", n_layers=3, prompt_len=96, n_decode=32),
+    # grouped-query attention, 32 query heads x 80 over 8 KV heads, a
+    # prompt long enough that every attention split holds many positions
+    "longctx_2l": dict(name="longctx", n_layers=2, prompt_len=1200, n_decode=16),
+    # 64 routed experts (top 6, softmax weights) + 2 shared, hidden 1408
+    "moe_2l": dict(name="moe", n_layers=2, prompt_len=48, n_decode=24),
+    # a narrow MoE with few experts: many routing decisions per second of oracle
+    "moe_narrow": dict(name="moe", n_layers=2, d_model=256, n_heads=4, n_kv_heads=4,
+                       head_dim=64, vocab_in=4096, vocab_out=4096, n_experts=8, top_k=2,
+                       n_shared_experts=1, expert_hidden=128, prompt_len=64, n_decode=48),
+    # GQA with two query heads per KV head and a head size of 64
+    "gqa2_narrow": dict(name="tiny", n_heads=8, n_kv_heads=4, head_dim=32, prompt_len=80,
+                        n_decode=40),
+}
+
+
+def _variant(key):
+    kw = dict(VARIANTS[key])
+    return _model(kw.pop("name"), **kw)
+
+
+def _moe_check(eng, o, cfg, positions):
+    """Routing at every listed position (prefill and decode) against the
+    oracle; returns the positions with an accepted near-tie difference."""
+    positions = list(positions)
+    ids = np.concatenate([eng.expert_ids(p, p + 1) for p in positions])
+    ids_or = np.stack([o.route[p][0] for p in positions])
+    r_or = [o.route[p][1] for p in positions]
+    where = {}
+    tied = [positions[i] for i in compare_routing(ids, ids_or, r_or, cfg.top_k, where)]
+    _say("routing near-ties (position: layer)", {positions[i]: l for i, l in where.items()})
+    return tied
+
+
+@pytest.mark.parametrize("key", sorted(VARIANTS))
+def test_variant_decode_parity(torch, kie, key):
+    cfg = _variant(key)
+    _say("variant parity", key)
+    W = _gpu_weights(torch, cfg)
+    Wn = weights_to_numpy(W)
+    prompt = make_prompt(cfg)
+    n = cfg.n_decode
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n)
+    assert eng.position == len(prompt) - 1 + n
+    assert np.all((toks >= 0) & (toks < cfg.vocab_out))
+    o, zo = _oracle_replay(cfg, Wn, prompt, toks)
+    P = len(prompt)
+    tied = _moe_check(eng, o, cfg, range(P - 1 + n)) if cfg.is_moe else []
+    rep = compare_steps(z, toks, zo, skip=[q - (P - 1) for q in tied if q >= P - 1])
+    _say(key, rep, "routing near-ties at positions", tied)
+    assert rep["pinned"] >= n // 2
+    _check_kv(eng, o, range(cfg.n_layers), [(0, P - 1 + n)], exclude=tied)
+    eng.close()
+
+
+def test_longctx_8192_prompt_attention(torch, kie):
+    """The long-context head layout (GQA 32 x 80 over 8 KV heads) with the
+    full 8192-token prompt and the full cache capacity, so the split-K
+    attention runs over its real span; two layers keep the oracle's batched
+    prefill to seconds."""
+    cfg = _model("longctx", n_layers=2, n_decode=8)
+    _say("longctx 8192: weights")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    n = cfg.n_decode
+    _say("longctx 8192: gpu run")
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n, max_seq=8192 + 256)
+    _say("longctx 8192: oracle replay")
+    o, zo = _oracle_replay(cfg.with_(max_seq=8192 + 256), weights_to_numpy(W), prompt, toks)
+    rep = compare_steps(z, toks, zo)
+    _say("longctx 8192", rep)
+    P = len(prompt)
+    _check_kv(eng, o, (0, 1), [(0, 64), (4000, 4100), (P - 80, P - 1 + n)])
+    eng.close()
+
+
+@pytest.mark.parametrize("name,prompt_len,n,layers", [
+    ("tp8share", 256, 8, (0, 12, 24)),
+    ("longctx", 256, 6, (0, 12, 24)),
+    ("moe", 8, 4, (0, 11, 23)),
+])
+def test_full_size_variant_parity_sampled(torch, kie, name, prompt_len, n, layers):
+    """Each other workload at full depth and width, with the cache capacity
+    of its full run (so the attention split layout is the real one), on a
+    prompt short enough for the oracle to replay every step."""
+    full = _model(name)
+    cfg = full.with_(prompt_len=prompt_len, n_decode=n)
+    cap = full.prompt_len + full.n_decode
+    _say(f"{name} full size: weights")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    _say(f"{name} full size: gpu run")
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n, max_seq=cap)
+    _say(f"{name} full size: oracle replay")
+    o = Oracle(cfg.with_(max_seq=cap), weights_to_numpy(W), cache_bytes=24 << 30,
+               kv_fp16=cfg.is_moe)
+    o.prefill(prompt)
+    _, zo = o.decode(n, force=toks)
+    P = len(prompt)
+    tied = _moe_check(eng, o, cfg, range(P - 1 + n)) if cfg.is_moe else []
+    rep = compare_steps(z, toks, zo, skip=[q - (P - 1) for q in tied if q >= P - 1])
+    _say(name, rep, "routing near-ties at positions", tied)
+    _check_kv(eng, o, layers, [(0, 1), (P // 2, P // 2 + 1), (P - 1, P - 1 + n)], exclude=tied)
     eng.close()

@@ -253,6 +253,49 @@ def test_batched_prefill_equals_sequential():
     np.testing.assert_allclose(za, zb, atol=1e-4)
 
 
+def test_moe_routing_record_is_per_position_and_prefill_independent():
+    """The routing record is keyed by position; batched prefill records the
+    same experts (and router logits, to rounding) as running the prompt
+    through the one-token step, and each decode step adds its position."""
+    cfg = SMALL_MOE.with_(prompt_len=9)
+    W = _np_weights(cfg, std=0.3)
+    prompt = make_prompt(cfg)
+    a = Oracle(cfg, W)
+    b = Oracle(cfg, W)
+    a.prefill(prompt, batched=True)
+    b.prefill(prompt, batched=False)
+    P = len(prompt)
+    assert sorted(a.route) == sorted(b.route) == list(range(P - 1))
+    for p in range(P - 1):
+        np.testing.assert_array_equal(a.route[p][0], b.route[p][0])
+        np.testing.assert_allclose(a.route[p][1], b.route[p][1], atol=1e-5)
+        assert a.route[p][0].shape == (cfg.n_layers, cfg.top_k)
+    a.decode(3)
+    assert sorted(a.route) == list(range(P + 2))
+    for i in range(3):
+        np.testing.assert_array_equal(a.route[P - 1 + i][0], a.expert_log[i])
+
+
+def test_routing_comparison_accepts_only_near_ties():
+    from tests.parity import compare_routing
+    r = np.array([[[5.0, 4.0, 3.0, 2.9995, 1.0]]])          # 3rd/4th logits 5e-4 apart
+    ok = np.array([[[0, 1, 2]]])
+    assert compare_routing(ok, ok, r, 3) == []
+    assert compare_routing(np.array([[[0, 1, 3]]]), ok, r, 3) == [0]   # near-tie swap
+    with pytest.raises(AssertionError):
+        compare_routing(np.array([[[0, 1, 4]]]), ok, r, 3)         # not a near tie
+    with pytest.raises(AssertionError):
+        compare_routing(np.array([[[1, 0, 2]]]), ok, r, 3)         # order of clear winners
+    r2 = np.array([[[5.0, 4.9995, 3.0, 1.0, 0.0]]])
+    assert compare_routing(np.array([[[1, 0, 2]]]), ok, r2, 3) == []   # order of tied pair
+    # a near-tie flip in layer 0 changes layer 1's input: layer 1 is not compared
+    r3 = np.concatenate([r, np.array([[[9.0, 0.0, 0.0, 0.0, 8.0]]])], axis=1)
+    both = np.array([[[0, 1, 2], [0, 4, 1]]])
+    where = {}
+    assert compare_routing(np.array([[[0, 1, 3], [1, 2, 3]]]), both, r3, 3, where) == [0]
+    assert where == {0: 0}
+
+
 def test_gqa_equals_mha_with_repeated_kv_rows():
     cfg = SMALL_GQA
     W = _np_weights(cfg, seed=5, std=0.3)
