@@ -6,8 +6,9 @@
  *   The pages describe a "persistent monokernel": one GPU-resident program
  *   that runs the whole decode path (matrix multiplies, attention,
  *   normalisation and sampling) and never hands control back to the CPU
- *   between tokens (page "Breaking the memory wall: 3,000 tokens/s on
- *   standard GPUs", agentlenshq.com, section "1. The Monokernel Runtime").
+ *   between tokens (page "Breaking the memory wall: 3,000 tokens/s
+ *   inference on standard GPUs", agentlenshq.com, section "1. The Monokernel
+ *   Runtime").
  *   They name the overheads it removes: ~4.5 us per kernel launch,
  *   host-side scheduling and CPU sampling, and grid-wide synchronisation
  *   (same page, section "Where the microseconds are lost").  kie_decode()

@@ -5,7 +5,7 @@ CPU oracle.  It draws random numbers and lays them out; it holds none of the
 decoder's arithmetic (no normalisation, attention, projection or sampling).
 
 The pages study single-request decode of a ~2B-parameter FP16 model
-(page "Breaking the memory wall: 3,000 tokens/s on standard GPUs",
+(page "Breaking the memory wall: 3,000 tokens/s inference on standard GPUs",
 agentlenshq.com, intro and section "The bottleneck: memory bandwidth, not
 compute").  They publish neither that model's architecture nor its weights,
 so every workload here is a synthetic stand-in with the stated shapes:

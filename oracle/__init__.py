@@ -10,7 +10,7 @@ What it computes, and where that comes from
 The pages describe the persistent monokernel as one GPU-resident program that
 runs the whole decode path — matrix multiplies, attention, normalisation and
 sampling — without handing control back to the CPU (page "Breaking the memory
-wall: 3,000 tokens/s on standard GPUs", agentlenshq.com, section
+wall: 3,000 tokens/s inference on standard GPUs", agentlenshq.com, section
 "1. The Monokernel Runtime").  The monokernel is a schedule, not an
 approximation: it must produce what a plain layer-by-layer decoder produces.
 This package is that plain decoder, written in numpy in the precision the

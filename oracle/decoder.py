@@ -7,7 +7,7 @@ Source of each step
 -------------------
 * Decode at batch 1 streams every active weight once per generated token and
   is bound by memory bandwidth (page "Breaking the memory wall: 3,000 tokens/s
-  on standard GPUs", section "The bottleneck: memory bandwidth, not
+  inference on standard GPUs", section "The bottleneck: memory bandwidth, not
   compute"); that is why the weights stay fp16 in memory here too and are
   only widened for the arithmetic.
 * The path consists of matrix multiplies, attention, normalisation and
