@@ -13,7 +13,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxGroup = 4;               // query heads per KV head
 constexpr int kMaxHeadDim = 128;           // 16 lanes x 8 fp16 per K/V row
 constexpr int kMaxActiveExperts = 16;      // top_k + shared
-constexpr int kBatch = 8;                  // GEMV: 16-byte loads per lane per batch
+constexpr int kBatch = 4;                  // GEMV: 16-byte loads per lane per batch
 constexpr int kPartCap = 2048;             // GEMV: per-block task partials in LDS (floats)
 constexpr int kGroups = 8;                 // grid barrier: arrival groups (one per XCD)
 constexpr int kGroupStride = 64;           // grid barrier: words between counters (256 B)
