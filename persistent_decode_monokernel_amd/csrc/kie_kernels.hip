@@ -1521,7 +1521,8 @@ __device__ __forceinline__ const Params& fresh(const Params* pp) {
 
 template <int G>
 __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restrict__ pp) {
-  extern __shared__ float smem[];
+  // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int flag;
   const int wg = blockIdx.x;
   GridSync gs;
@@ -1612,7 +1613,8 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
 enum StageId : int { kSQkv, kSAttn, kSMerge, kSO, kSGateUp, kSDown, kSRouter, kSMoeGateUp, kSMoeDown, kSLm };
 
 __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage, int l) {
-  extern __shared__ float smem[];
+  // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int flag;
   const Lds s = lds_carve(p, smem);
   const Ctl c = make_ctl(p, &flag);
@@ -1668,7 +1670,8 @@ __global__ void step_end_kernel(Params p) {
 // ---- inspection kernels
 __global__ __launch_bounds__(kThreads, 1) void gemv_kernel(const __half* w, const float* x, float* y,
                                                            int rows, int cols, int n_wg) {
-  extern __shared__ float smem[];
+  // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   float* h = smem;
   float* part = smem + ((cols + 63) & ~63);
   float* sums = part + kPartCap;
