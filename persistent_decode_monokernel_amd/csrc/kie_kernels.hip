@@ -534,79 +534,119 @@ __device__ __forceinline__ bool wg_all(bool ok, int* flag) {
 
 constexpr int kGatherPer = 8;    // words per thread per pass
 
+// One thread's share of a gather pass: up to kGatherPer arena words, their
+// expected epochs and LDS destinations, and which of them are still pending.
+struct GatherSlots {
+  unsigned pending;
+  unsigned off[kGatherPer];
+  unsigned want[kGatherPer];
+  lds_float* dst[kGatherPer];       // 32-bit LDS addresses
+};
+
+template <int NR>
+__device__ __forceinline__ GatherSlots gather_slots(const LLRange (&rg)[NR], int total, int seg) {
+  GatherSlots S;
+  S.pending = 0;
+#pragma unroll
+  for (int k = 0; k < kGatherPer; ++k) {
+    int i = seg + (int)threadIdx.x + k * kThreads;
+    S.off[k] = kOffNone;
+    S.want[k] = 0u;
+    S.dst[k] = nullptr;
+    if (i < total) {
+      S.pending |= 1u << k;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (i >= 0 && i < rg[r].n) {
+          S.off[k] = (unsigned)(rg[r].src + i) * 8u;
+          S.want[k] = rg[r].want;
+          S.dst[k] = (lds_float*)(rg[r].dst + i);
+        }
+        i -= rg[r].n;
+      }
+    }
+  }
+  return S;
+}
+
+__device__ __forceinline__ void gather_issue(Rsrc arena, const GatherSlots& S, u32x2 (&v)[kGatherPer]) {
+#pragma unroll
+  for (int k = 0; k < kGatherPer; ++k) v[k] = ld_ll(arena, ((S.pending >> k) & 1u) ? S.off[k] : kOffNone);
+}
+
+__device__ __forceinline__ void gather_take(GatherSlots& S, const u32x2 (&v)[kGatherPer]) {
+#pragma unroll
+  for (int k = 0; k < kGatherPer; ++k) {
+    if (((S.pending >> k) & 1u) && v[k].y == S.want[k]) {
+      *S.dst[k] = __uint_as_float(v[k].x);
+      S.pending &= ~(1u << k);
+    }
+  }
+}
+
+// Polls until every slot is valid; false on timeout or a reported error.
+__device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherSlots& S, const Ctl& c) {
+  long long t0 = 0;
+  int spins = 0;
+  while (S.pending) {
+    ++spins;
+    if ((spins & 15) == 1) {
+      if (spins == 1) t0 = wall_clock64();
+      if (__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+      if (wall_clock64() - t0 > c.ticks) {
+        set_timeout(c.err);
+        return false;
+      }
+    }
+    if (c.spin_limit > 0 && spins >= c.spin_limit) {
+      set_timeout(c.err);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    u32x2 v[kGatherPer];
+    gather_issue(arena, S, v);
+    gather_take(S, v);
+  }
+  return true;
+}
+
 // Copies up to NR ranges of the arena into LDS, waiting until every word
 // carries its range's epoch.  Thread t owns words t, t + kThreads, ... of
 // the concatenated ranges and re-reads only the ones not yet valid; loads
-// are issued for all of them at once.  Returns false (uniformly) when a
-// wait passes the timeout or another workgroup reported an error.
-template <int NR>
-__device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c) {
+// are issued for all of them at once.
+//
+// `issue()` is called once, right after the first poll loads are issued and
+// before their results are used: loads it issues (the next weights) queue
+// behind the first poll instead of in front of it, so that poll returns at
+// the fabric's latency rather than after the prefetch has landed (loads
+// return in issue order).  The first round is written out on its own so the
+// compiler sees a single issue order there.  Returns false (uniformly) when
+// a wait passes the timeout or another workgroup reported an error.
+template <int NR, class Issue>
+__device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c,
+                                          Issue&& issue) {
   const Rsrc arena = arena_rsrc(p);
   int total = 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) total += rg[r].n;
-  bool ok = true;
-  for (int seg = 0; seg < total && ok; seg += kGatherPer * kThreads) {
-    unsigned pending = 0;
-    unsigned off[kGatherPer];
-    unsigned want[kGatherPer];
-    lds_float* dst[kGatherPer];       // 32-bit LDS addresses
-#pragma unroll
-    for (int k = 0; k < kGatherPer; ++k) {
-      int i = seg + (int)threadIdx.x + k * kThreads;
-      off[k] = kOffNone;
-      want[k] = 0u;
-      dst[k] = nullptr;
-      if (i < total) {
-        pending |= 1u << k;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if (i >= 0 && i < rg[r].n) {
-            off[k] = (unsigned)(rg[r].src + i) * 8u;
-            want[k] = rg[r].want;
-            dst[k] = (lds_float*)(rg[r].dst + i);
-          }
-          i -= rg[r].n;
-        }
-      }
-    }
-    long long t0 = 0;
-    int spins = 0;
-    while (pending) {
-      u32x2 v[kGatherPer];
-#pragma unroll
-      for (int k = 0; k < kGatherPer; ++k) v[k] = ld_ll(arena, ((pending >> k) & 1u) ? off[k] : kOffNone);
-#pragma unroll
-      for (int k = 0; k < kGatherPer; ++k) {
-        if (((pending >> k) & 1u) && v[k].y == want[k]) {
-          *dst[k] = __uint_as_float(v[k].x);
-          pending &= ~(1u << k);
-        }
-      }
-      if (pending) {
-        ++spins;
-        if ((spins & 15) == 1) {
-          if (spins == 1) t0 = wall_clock64();
-          if (__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            ok = false;
-            break;
-          }
-          if (wall_clock64() - t0 > c.ticks) {
-            set_timeout(c.err);
-            ok = false;
-            break;
-          }
-        }
-        if (c.spin_limit > 0 && spins >= c.spin_limit) {
-          set_timeout(c.err);
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
+  GatherSlots S = gather_slots(rg, total, 0);
+  {
+    u32x2 v[kGatherPer];
+    gather_issue(arena, S, v);
+    issue();
+    gather_take(S, v);
+  }
+  bool ok = gather_wait(p, arena, S, c);
+  for (int seg = kGatherPer * kThreads; seg < total && ok; seg += kGatherPer * kThreads) {
+    S = gather_slots(rg, total, seg);
+    ok = gather_wait(p, arena, S, c);
   }
   return wg_all(ok, c.flag);
+}
+
+template <int NR>
+__device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c) {
+  return ll_gather(p, rg, c, [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -636,14 +676,19 @@ __device__ __forceinline__ Lds lds_carve(const Params& p, float* smem) {
 // activations, for up to kGainPer * kThreads elements.
 constexpr int kGainPer = 8;
 struct GainPre {
-  float g[kGainPer];
+  unsigned short g[kGainPer];      // raw fp16 bits
 };
+// Branch-free buffer loads: lanes past d use an out-of-range offset and read
+// zero.  A guarded load (or a pointer the compiler cannot prove global)
+// becomes a flat load followed by a wait for every outstanding load, which
+// would drain the weight prefetch issued just before.
 __device__ __forceinline__ GainPre gain_prefetch(const __half* gain, int d) {
+  const Rsrc r = make_rsrc(gain, (size_t)d * 2);
   GainPre G;
 #pragma unroll
   for (int k = 0; k < kGainPer; ++k) {
     const int i = threadIdx.x + k * kThreads;
-    G.g[k] = i < d ? __half2float(gain[i]) : 0.f;
+    G.g[k] = __builtin_amdgcn_raw_buffer_load_b16(r, i < d ? (unsigned)i * 2u : kOffNone, 0, 0);
   }
   return G;
 }
@@ -660,7 +705,7 @@ __device__ __forceinline__ void rmsnorm_lds(const Params& p, const __half* gain,
 #pragma unroll
   for (int k = 0; k < kGainPer; ++k) {
     const int i = threadIdx.x + k * kThreads;
-    if (i < d) h[i] = h[i] * inv * G.g[k];
+    if (i < d) h[i] = h[i] * inv * __half2float(__ushort_as_half(G.g[k]));
   }
   for (int i = threadIdx.x + kGainPer * kThreads; i < d; i += kThreads)
     h[i] = h[i] * inv * __half2float(gain[i]);
@@ -797,9 +842,16 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
                                           int& tok, Resolve&& resolve) {
   const GemvWork g = qkv_work(p, wg);
   const QkvAddr addr = qkv_addr(p, l);
-  const WPre pre = gemv_prefetch(g, addr);
   const __half* gain = layer(p, l).attn_norm;
-  const GainPre G = gain_prefetch(gain, p.d);
+  WPre pre;
+  GainPre G;
+  auto issue = [&]() {
+    pre = gemv_prefetch(g, addr);
+    G = gain_prefetch(gain, p.d);
+  };
+  // Layer 0 waits for the grid barrier or reads the embedding: prefetch
+  // first.  Later layers prefetch behind the first poll of x.
+  if (l == 0) issue();
   if (wait_first) {
     if (!grid_wait(gs, c.flag)) return false;
     tok = resolve();
@@ -811,7 +863,7 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
     }
   } else if (g.r0 < g.r1) {
     const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l - 1, kSlotXDown)}};
-    if (!ll_gather(p, rg, c)) return false;
+    if (!ll_gather(p, rg, c, issue)) return false;
   }
   mark(tr);
   if (g.r0 >= g.r1) {
@@ -1216,7 +1268,7 @@ __device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, co
                                             int wg, Lds s, const Ctl& c, Tracer& tr) {
   const GemvWork g = o_work(p, wg);
   const RowAddr addr = o_addr(p, l);
-  const WPre pre = gemv_prefetch(g, addr);
+  WPre pre;
   const int qd = p.H * p.hd;
   const int nown = g.r1 - g.r0;
   if (l == 0) {
@@ -1225,7 +1277,7 @@ __device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, co
   const LLRange rg[2] = {{p.off_o, qd, s.h, ll_flag(p, step, l, kSlotO)},
                          {p.off_x + g.r0, l == 0 ? 0 : nown, s.xown,
                           l == 0 ? 0u : ll_flag(p, step, l - 1, kSlotXDown)}};
-  if (!ll_gather(p, rg, c)) return false;
+  if (!ll_gather(p, rg, c, [&]() { pre = gemv_prefetch(g, addr); })) return false;
   mark(tr);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXO);
@@ -1253,16 +1305,20 @@ __device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, i
                                              const Ctl& c, Tracer& tr) {
   const GemvWork g = gu_work(p, wg);
   const PairAddr addr = gu_addr(p, l);
-  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
     mark(tr);
     mark(tr);
     return true;
   }
   const __half* gain = layer(p, l).ffn_norm;
-  const GainPre G = gain_prefetch(gain, p.d);
+  WPre pre;
+  GainPre G;
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c)) return false;
+  if (!ll_gather(p, rg, c, [&]() {
+        pre = gemv_prefetch(g, addr);
+        G = gain_prefetch(gain, p.d);
+      }))
+    return false;
   mark(tr);
   rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
@@ -1285,11 +1341,11 @@ __device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int
                                            const Ctl& c, Tracer& tr) {
   const GemvWork g = down_work(p, wg);
   const RowAddr addr = down_addr(p, l);
-  const WPre pre = gemv_prefetch(g, addr);
+  WPre pre;
   const int nown = g.r1 - g.r0;
   const LLRange rg[2] = {{p.off_u, p.F, s.h, ll_flag(p, step, l, kSlotU)},
                          {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c)) return false;
+  if (!ll_gather(p, rg, c, [&]() { pre = gemv_prefetch(g, addr); })) return false;
   mark(tr);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXDown);
@@ -1462,15 +1518,19 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
                                              Tracer& tr) {
   const GemvWork g = lm_work(p, wg);
   const RowAddr addr{mat_rsrc(p.lm_head, p.Vout, p.d), p.d};
-  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
     mark(tr);
     mark(tr);
     return true;
   }
-  const GainPre G = gain_prefetch(p.final_norm, p.d);
+  WPre pre;
+  GainPre G;
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, p.L - 1, kSlotXDown)}};
-  if (!ll_gather(p, rg, c)) return false;
+  if (!ll_gather(p, rg, c, [&]() {
+        pre = gemv_prefetch(g, addr);
+        G = gain_prefetch(p.final_norm, p.d);
+      }))
+    return false;
   mark(tr);
   rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
   mark(tr);
