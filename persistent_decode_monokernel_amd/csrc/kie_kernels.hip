@@ -161,19 +161,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Workgroup sum in a fixed order: every workgroup computes bit-identical
-// results from identical inputs.  `red` holds kWaves floats of LDS.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += red[i];
-  return s;
-}
-
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
 // Order-preserving map of a float to 32 bits, packed above the complemented
@@ -299,7 +286,7 @@ __device__ __forceinline__ bool grid_wait(GridSync& g, int* flag) {
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    *flag = ok;
+    if (!ok) *flag = 0;               // the flag is 1 until a failure (see wg_all)
   }
   __syncthreads();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -523,10 +510,9 @@ __device__ __forceinline__ Ctl make_ctl(const Params& p, int* flag) {
 }
 
 // Workgroup-uniform AND of `ok` (every thread passes its own value).
+// The flag is set to 1 when the kernel starts and only ever cleared on a
+// failure, after which every thread leaves the kernel; one barrier suffices.
 __device__ __forceinline__ bool wg_all(bool ok, int* flag) {
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = 1;
-  __syncthreads();
   if (!ok) *flag = 0;
   __syncthreads();
   return *flag != 0;
@@ -693,23 +679,37 @@ __device__ __forceinline__ GainPre gain_prefetch(const __half* gain, int d) {
   return G;
 }
 
-// RMSNorm of the d values in h (LDS), in place, recomputed by every
-// workgroup in a fixed order: h = v / sqrt(mean(v^2) + eps) * gain.
-__device__ __forceinline__ void rmsnorm_lds(const Params& p, const __half* gain, const GainPre& G,
-                                            float* h, float* red) {
+// RMSNorm folded into the GEMV that consumes it: rms(v) * gain = (v * gain)
+// / sqrt(mean(v^2) + eps), and the divisor is one scalar, so it scales the
+// GEMV's row sums instead of every input.  One pass over h (LDS, in place)
+// multiplies by the gain and accumulates the sum of squares of the raw
+// values in a fixed order; returns 1 / sqrt(mean(v^2) + eps), the same in
+// every thread.
+__device__ __forceinline__ float rmsnorm_lds(const Params& p, const __half* gain, const GainPre& G,
+                                             float* h, float* red) {
   const int d = p.d;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += kThreads) ss = fmaf(h[i], h[i], ss);
-  ss = block_sum(ss, red);
-  const float inv = 1.0f / sqrtf(ss / (float)d + p.eps);
 #pragma unroll
   for (int k = 0; k < kGainPer; ++k) {
     const int i = threadIdx.x + k * kThreads;
-    if (i < d) h[i] = h[i] * inv * __half2float(__ushort_as_half(G.g[k]));
+    if (i < d) {
+      const float v = h[i];
+      ss = fmaf(v, v, ss);
+      h[i] = v * __half2float(__ushort_as_half(G.g[k]));
+    }
   }
-  for (int i = threadIdx.x + kGainPer * kThreads; i < d; i += kThreads)
-    h[i] = h[i] * inv * __half2float(gain[i]);
+  for (int i = threadIdx.x + kGainPer * kThreads; i < d; i += kThreads) {
+    const float v = h[i];
+    ss = fmaf(v, v, ss);
+    h[i] = v * __half2float(gain[i]);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += red[w];
+  return 1.0f / sqrtf(tot / (float)d + p.eps);
 }
 
 // Appends one clock stamp to the workgroup's trace (traced steps only).
@@ -870,12 +870,13 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
     mark(tr);
     return true;
   }
-  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotQkv);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
-                   for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_qkv + b0 + i, sums[i], f);
+                   for (int i = threadIdx.x; i < n; i += kThreads)
+                     ll_put(p, p.off_qkv + b0 + i, sums[i] * inv, f);
                  });
   return true;
 }
@@ -1320,12 +1321,12 @@ __device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, i
       }))
     return false;
   mark(tr);
-  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotU);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; 2 * i < n; i += kThreads)
-      ll_put(p, p.off_u + (b0 >> 1) + i, silu(sums[2 * i]) * sums[2 * i + 1], f);
+      ll_put(p, p.off_u + (b0 >> 1) + i, silu(sums[2 * i] * inv) * (sums[2 * i + 1] * inv), f);
   });
   return true;
 }
@@ -1384,11 +1385,11 @@ __device__ __forceinline__ bool stage_router(const Params& p, int step, int l, i
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
   if (!ll_gather(p, rg, c)) return false;
   mark(tr);
-  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotRouter);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
-    for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_router + b0 + i, sums[i], f);
+    for (int i = threadIdx.x; i < n; i += kThreads) ll_put(p, p.off_router + b0 + i, sums[i] * inv, f);
   });
   return true;
 }
@@ -1450,7 +1451,7 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
     mark(tr);
     return true;
   }
-  rmsnorm_lds(p, gain, G, s.h, s.red);
+  const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
   const int Fe = p.Fe, ne = p.E + p.nshared;
   const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
@@ -1458,7 +1459,7 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
   gemv_run<false>(g, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
     for (int i = threadIdx.x; 2 * i < n; i += kThreads) {
       const int ff = (b0 >> 1) + i;
-      ll_put(p, p.off_u + ff, wts[ff / Fe] * silu(sums[2 * i]) * sums[2 * i + 1], f);
+      ll_put(p, p.off_u + ff, wts[ff / Fe] * silu(sums[2 * i] * inv) * (sums[2 * i + 1] * inv), f);
     }
   });
   return true;
@@ -1532,14 +1533,14 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
       }))
     return false;
   mark(tr);
-  rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
+  const float inv = rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
   mark(tr);
   float* logits = p.out_logits ? p.out_logits + (size_t)step * p.Vout : nullptr;
   unsigned long long best = 0ull;
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
                    for (int i = threadIdx.x; i < n; i += kThreads) {
-                     const float v = sums[i];
+                     const float v = sums[i] * inv;
                      if (logits) logits[b0 + i] = v;
                      const unsigned long long k = argmax_key(v, b0 + i);
                      best = k > best ? k : best;
@@ -1584,6 +1585,8 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int flag;
+  if (threadIdx.x == 0) flag = 1;
+  __syncthreads();
   const int wg = blockIdx.x;
   GridSync gs;
   Lds s;
@@ -1676,6 +1679,8 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage,
   // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ int flag;
+  if (threadIdx.x == 0) flag = 1;
+  __syncthreads();
   const Lds s = lds_carve(p, smem);
   const Ctl c = make_ctl(p, &flag);
   const int wg = blockIdx.x;
@@ -1751,7 +1756,10 @@ __global__ __launch_bounds__(kThreads, 1) void barrier_test_kernel(unsigned* bar
   __shared__ int bad;
   const unsigned nwg = gridDim.x;
   GridSync gs = make_sync(bar, err, nwg, ticks, spin_limit);
-  if (threadIdx.x == 0) bad = 0;
+  if (threadIdx.x == 0) {
+    bad = 0;
+    flag = 1;
+  }
   __syncthreads();
   for (int r = 1; r <= rounds; ++r) {
     if (threadIdx.x == 0) st_cu(slots + blockIdx.x, (unsigned)r);
