@@ -366,21 +366,30 @@ __device__ __forceinline__ WBatch wload(const Addr& addr, const GemvWork& g, int
   return B;
 }
 
+// The kBatch tasks of a batch are independent: their dot products and wave
+// reductions are written as separate chains, with no branch between them,
+// so the compiler interleaves them instead of running one latency-bound
+// chain per task.  Tasks past `tend` and lanes past the row end hold zero
+// weights (their loads used an out-of-range offset), so only the final
+// partial store is conditional.
 __device__ __forceinline__ void wconsume(const WBatch& B, const float* h, const GemvWork& g, int t,
                                          int tend, float* part) {
   const int lane = threadIdx.x & 63;
   const float4* h4 = reinterpret_cast<const float4*>(h);
   int s = t % g.ks;
+  float a[kBatch];
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
-    if (t + i < tend) {                       // wave-uniform
-      // lanes past the row end hold zero weights; clamp their LDS index
-      const int c = min(s * 64 + lane, g.nch - 1);
-      float a = dot8(B.w[i], h4[2 * c], h4[2 * c + 1], 0.f);
-      a = wave_sum(a);
-      if (lane == 0) part[t + i] = a;
-    }
+    const int c = min(s * 64 + lane, g.nch - 1);     // clamp the LDS index of lanes past the row end
+    a[i] = dot8(B.w[i], h4[2 * c], h4[2 * c + 1], 0.f);
     if (++s == g.ks) s = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) a[i] = wave_sum(a[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (t + i < tend) part[t + i] = a[i];
   }
   __builtin_amdgcn_sched_barrier(0);
 }
