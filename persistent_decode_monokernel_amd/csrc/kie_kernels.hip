@@ -1141,20 +1141,60 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
     }
   };
 
+  // The kAU positions a 16-lane group holds per block are folded into the
+  // online softmax together: their scores are independent chains, then one
+  // new maximum and one rescale of the accumulators.  Positions past pend
+  // (zero K/V rows) get weight exactly zero.  Same arithmetic as one position
+  // at a time, in a different fixed order.
+  auto consume_block = [&](const u32x4 (&kb)[kAU], const u32x4 (&vb)[kAU], const bool (&ok)[kAU]) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float sc[kAU];
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) {
+        float kf[8];
+        unpack8(kb[u], kf);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qr[h][e], kf[e], d);
+        sc[u] = d;
+      }
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) sc[u] = group16_sum(sc[u]);
+      float mn = m[h];
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) mn = ok[u] ? fmaxf(mn, sc[u]) : mn;
+      const float corr = exp2f(m[h] - mn);
+      float pw[kAU];
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) pw[u] = ok[u] ? exp2f(sc[u] - mn) : 0.f;
+      float ls = lsum[h] * corr;
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) ls += pw[u];
+      lsum[h] = ls;
+      float av[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = acc[h][e] * corr;
+#pragma unroll
+      for (int u = 0; u < kAU; ++u) {
+        float vf[8];
+        unpack8(vb[u], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = fmaf(pw[u], vf[e], av[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = av[e];
+      m[h] = mn;
+    }
+  };
+
   for (int base = p0; base < pend; base += kAttnStride * kAU) {
     if (base != p0) kv_load_step(p, rk, rv, base, pend, kr, vr);
+    // a 16-lane group is wholly in or out, and its sums stay in the group
+    bool ok[kAU];
 #pragma unroll
-    for (int u = 0; u < kAU; ++u) {
-      const int j0 = base + u * kAttnStride + wave * 4;   // first position of this wave's step
-      if (j0 < pend) {                                    // wave-uniform
-        const int j = j0 + grp;
-        float kf[8], vf[8];
-        unpack8(kr[u], kf);
-        unpack8(vr[u], vf);
-        // a 16-lane group is wholly in or out, and its sums stay in the group
-        if (j < pend) consume(kf, vf);
-      }
-    }
+    for (int u = 0; u < kAU; ++u) ok[u] = base + u * kAttnStride + wave * 4 + grp < pend;
+    consume_block(kr, vr, ok);
   }
   if (has_new && wave == 0 && grp == 0) {
     float kf[8], vf[8];
