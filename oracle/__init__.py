@@ -23,12 +23,18 @@ embeddings, greedy decoding and softmax top-k routing with shared experts;
 every point they leave open is read the plain (Llama-style) way, stated at
 the function that makes the choice.
 
+``sampling`` defines temperature sampling (a draw from softmax(z / T) by the
+Gumbel-max method, with Philox4x64-10 counter-based random numbers) exactly
+as the decode kernel computes it.
+
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, invariants, special cases and brute force; none is
-"parity unpinned".
+against closed forms, invariants, special cases, brute force and library
+routines; none is "parity unpinned".
 """
 from .decoder import (Oracle, rmsnorm, rope_cos_sin, rope, softmax, attend,
                       silu, swiglu, moe_route, moe_ffn, argmax_first)
+from .sampling import philox4x64, uniforms, gumbel, sample_keys, sample_token
 
 __all__ = ["Oracle", "rmsnorm", "rope_cos_sin", "rope", "softmax", "attend",
-           "silu", "swiglu", "moe_route", "moe_ffn", "argmax_first"]
+           "silu", "swiglu", "moe_route", "moe_ffn", "argmax_first",
+           "philox4x64", "uniforms", "gumbel", "sample_keys", "sample_token"]
