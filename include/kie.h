@@ -151,6 +151,23 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * KIE_ERR_CONTEXT_OVERFLOW if position + n_steps > max_seq. */
 int kie_decode(kie_handle *h, int32_t n_steps, int32_t *out_tokens, float *out_logits);
 
+/* As kie_decode, but each step draws its token from softmax(z / temperature)
+ * instead of taking the argmax: sampling inside the monokernel (page
+ * "Breaking the memory wall: 3,000 tokens/s inference on standard GPUs",
+ * section "1. The Monokernel Runtime").  The draw is the Gumbel-max method:
+ * the token is the first maximum over i of the float32 key
+ * z_i / temperature - log(-log(u_i)), formed in float64, where u_i is the
+ * top 53 bits (plus half a bin) of word i mod 4 of the Philox4x64-10 block
+ * for counter (position, i div 4, 0, 0) and key (seed, 0); `position` is
+ * the position of the step's input token.  So a (seed, position) pair
+ * always gives the same draw, and decode(a); decode(b) equals decode(a+b).
+ * temperature == 0 is greedy decoding (identical to kie_decode);
+ * KIE_ERR_INVALID_ARG if it is negative, infinite or NaN.  out_logits, if
+ * given, receives the logits z (not the keys).  Other arguments and errors
+ * as kie_decode. */
+int kie_decode_sampled(kie_handle *h, int32_t n_steps, uint64_t seed, float temperature,
+                       int32_t *out_tokens, float *out_logits);
+
 /* Drops the context: position 0, no pending token (KV contents are simply
  * overwritten by the next prefill).  Also clears a broken state. */
 int kie_reset(kie_handle *h);

@@ -1561,6 +1561,50 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
 // reduces its rows to one packed key and folds it into the step's slot with
 // a 64-bit atomic max (order independent, so deterministic).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Temperature sampling.  The pages put sampling inside the monokernel ("1. The
+// Monokernel Runtime"); a step draws its token from softmax(z / T) by the
+// Gumbel-max method: token = first argmax of z_i / T + g_i with Gumbel noise
+// g_i = -log(-log u_i), so the draw folds into the same packed 64-bit argmax
+// as greedy decoding.  u_i comes from Philox4x64-10 (Salmon et al., "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011): word i mod 4 of the block
+// for counter (pos, i div 4, 0, 0) and key (seed, 0), top 53 bits, centred
+// in their bin so u is never 0 or 1.  The key is formed in float64 and
+// rounded once to float32.
+// ---------------------------------------------------------------------------
+constexpr unsigned long long kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr unsigned long long kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr unsigned long long kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr unsigned long long kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+// Word `w` (0..3) of the Philox4x64-10 block for counter (c0, c1, 0, 0) and
+// key (k0, 0).
+__device__ __forceinline__ unsigned long long philox4x64_word(unsigned long long c0, unsigned long long c1,
+                                                              unsigned long long k0, int w) {
+  unsigned long long x0 = c0, x1 = c1, x2 = 0ull, x3 = 0ull, k1 = 0ull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long hi0 = __umul64hi(kPhiloxM0, x0), lo0 = kPhiloxM0 * x0;
+    const unsigned long long hi1 = __umul64hi(kPhiloxM1, x2), lo1 = kPhiloxM1 * x2;
+    const unsigned long long n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+    x0 = n0;
+    x1 = lo1;
+    x2 = n2;
+    x3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return w == 0 ? x0 : w == 1 ? x1 : w == 2 ? x2 : x3;
+}
+
+// float32 sampling key of logit v at vocabulary index i, decode position pos.
+__device__ __forceinline__ float sample_key(float v, float temperature, unsigned long long seed, int pos, int i) {
+  const unsigned long long w = philox4x64_word((unsigned long long)pos, (unsigned long long)(i >> 2), seed, i & 3);
+  const double u = ((double)(w >> 11) + 0.5) * 0x1p-53;
+  const double g = -log(-log(u));
+  return (float)((double)v / (double)temperature + g);
+}
+
 __device__ __forceinline__ GemvWork lm_work(const Params& p, int wg) {
   return gemv_work(p.Vout, p.d, p.n_wg, wg, false);
 }
@@ -1585,13 +1629,16 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
   const float inv = rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
   mark(tr);
   float* logits = p.out_logits ? p.out_logits + (size_t)step * p.Vout : nullptr;
+  const bool sample = p.sample != 0;
+  const int pos = p.pos0 + step;           // position of this step's input token
   unsigned long long best = 0ull;
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
                    for (int i = threadIdx.x; i < n; i += kThreads) {
                      const float v = sums[i] * inv;
                      if (logits) logits[b0 + i] = v;
-                     const unsigned long long k = argmax_key(v, b0 + i);
+                     const float key = sample ? sample_key(v, p.temperature, p.seed, pos, b0 + i) : v;
+                     const unsigned long long k = argmax_key(key, b0 + i);
                      best = k > best ? k : best;
                    }
                  });

@@ -73,6 +73,10 @@ struct Params {
   int spin_limit;               // > 0: cap on polls per wait (forced-watchdog tests)
   unsigned long long* trace;    // [n_wg][kTraceEvents] barrier clock stamps, or nullptr
   int trace_step;               // the decode step that is traced
+  // ---- per call: how a decode step picks its token
+  int sample;                   // 0: greedy argmax; 1: temperature sampling (Gumbel-max)
+  float temperature;            // > 0 when sampling
+  unsigned long long seed;      // sampling key (Philox4x64 key word 0)
 };
 
 // Host-visible launchers implemented next to the kernels.

@@ -448,8 +448,27 @@ int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
   return KIE_OK;
 }
 
+namespace {
+int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, bool sample,
+                 float temperature, uint64_t seed);
+}  // namespace
+
 int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits) {
   g_err.clear();
+  return decode_steps(h, n, out_tokens, out_logits, false, 0.f, 0ull);
+}
+
+int kie_decode_sampled(kie_handle* h, int32_t n, uint64_t seed, float temperature, int32_t* out_tokens,
+                       float* out_logits) {
+  g_err.clear();
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(KIE_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  return decode_steps(h, n, out_tokens, out_logits, temperature > 0.f, temperature, seed);
+}
+
+namespace {
+int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, bool sample,
+                 float temperature, uint64_t seed) {
   if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
   if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
   if (n < 0) return fail(KIE_ERR_INVALID_ARG, "n_steps < 0");
@@ -469,6 +488,9 @@ int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits)
   p.out_tokens = out_tokens;
   p.out_logits = out_logits;
   p.trace_step = n > 1 ? 1 : 0;
+  p.sample = sample ? 1 : 0;
+  p.temperature = sample ? temperature : 0.f;
+  p.seed = sample ? (unsigned long long)seed : 0ull;
   rc = run_steps(h, p);
   if (rc) return rc;
   h->pos += n;
@@ -483,6 +505,7 @@ int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits)
   }
   return KIE_OK;
 }
+}  // namespace
 
 int kie_reset(kie_handle* h) {
   g_err.clear();

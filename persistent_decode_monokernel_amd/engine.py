@@ -86,11 +86,23 @@ class Engine:
         lp = out_logits.data_ptr() if out_logits is not None else None
         check(self.lib.kie_decode(self.h, int(n), tp, lp), "kie_decode")
 
-    def decode(self, n: int, logits: bool = True):
+    def decode_sampled_into(self, n: int, seed: int, temperature: float, out_tokens: Optional[torch.Tensor],
+                            out_logits: Optional[torch.Tensor] = None) -> None:
+        """kie_decode_sampled: tokens drawn from softmax(z / temperature)."""
+        tp = out_tokens.data_ptr() if out_tokens is not None else None
+        lp = out_logits.data_ptr() if out_logits is not None else None
+        check(self.lib.kie_decode_sampled(self.h, int(n), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                          ctypes.c_float(float(temperature)), tp, lp), "kie_decode_sampled")
+
+    def decode(self, n: int, logits: bool = True, seed: Optional[int] = None, temperature: float = 0.0):
+        """n decode steps; greedy unless a seed and a temperature > 0 are given."""
         dev = self._weights["tok_emb"].device
         toks = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
         lg = torch.empty((max(n, 1), self.model.vocab_out), dtype=torch.float32, device=dev) if logits else None
-        self.decode_into(n, toks, lg)
+        if seed is None:
+            self.decode_into(n, toks, lg)
+        else:
+            self.decode_sampled_into(n, seed, temperature, toks, lg)
         return toks[:n], (lg[:n] if lg is not None else None)
 
     def reset(self) -> None:

@@ -120,3 +120,45 @@ def compare_routing(ids_gpu: np.ndarray, ids_or: np.ndarray, router_or, top_k: i
                 if where is not None:
                     where[i] = l
     return sorted(tied)
+
+
+# Sampled decode.  The draw is an integer decision taken from floating point
+# (keys z / T + g rounded to float32), so the kernel's token is checked
+# against the oracle's sampler applied to the kernel's own logits, where the
+# top-2 key margin clears the last-ulp differences of the float64 log
+# (libm on the host, the device math library on the GPU); the kernel's logits
+# are checked against the oracle's as for greedy decoding; and where the
+# oracle's own keys have a top-2 margin wider than twice the logit tolerance
+# over T, the kernel's token must also equal the oracle's own draw.
+KEY_MARGIN = 1e-5
+
+
+def compare_sampled_steps(z_gpu: np.ndarray, tok_gpu: np.ndarray, z_or: np.ndarray, temperature: float,
+                          seed: int, pos0: int):
+    from oracle.sampling import sample_keys
+    n = len(tok_gpu)
+    pinned = unpinned = cross = 0
+    worst = 0.0
+    for i in range(n):
+        zo = z_or[i].astype(np.float64)
+        zg = z_gpu[i].astype(np.float64)
+        err = float(np.max(np.abs(zg - zo)))
+        worst = max(worst, err)
+        assert err <= ABS_TOL, f"step {i}: max |dz| = {err:.3e} > {ABS_TOL}"
+        assert err <= REL_RANGE_TOL * float(zo.max() - zo.min()), f"step {i}: logits range"
+        keys = sample_keys(z_gpu[i], temperature, seed, pos0 + i).astype(np.float64)
+        order = np.argsort(-keys, kind="stable")
+        top, second = keys[order[0]], keys[order[1]]
+        if top - second > KEY_MARGIN * max(1.0, abs(top)):
+            pinned += 1
+            assert int(tok_gpu[i]) == int(order[0]), (
+                f"step {i}: gpu token {int(tok_gpu[i])} != draw {int(order[0])} from the gpu logits")
+        else:
+            unpinned += 1
+            assert int(tok_gpu[i]) in (int(order[0]), int(order[1])), f"step {i}: token not a top-2 key"
+        ko = sample_keys(z_or[i], temperature, seed, pos0 + i).astype(np.float64)
+        oo = np.argsort(-ko, kind="stable")
+        if ko[oo[0]] - ko[oo[1]] > 2.0 * 2.0 * ABS_TOL / temperature:
+            cross += 1
+            assert int(tok_gpu[i]) == int(oo[0]), f"step {i}: gpu token differs from the oracle's own draw"
+    return {"steps": n, "pinned": pinned, "unpinned": unpinned, "cross_checked": cross, "worst_abs": worst}

@@ -95,3 +95,15 @@ def test_null_handle_calls_are_rejected():
     p = ctypes.c_int32()
     assert lib.kie_get_position(None, ctypes.byref(p)) == -1
     lib.kie_destroy(None)                       # allowed
+
+
+def test_sampled_decode_validates_arguments_on_the_host():
+    # rejected before anything touches a device: no GPU needed
+    lib = _lib.load()
+    for t in (-1.0, float("nan"), float("inf")):
+        rc = lib.kie_decode_sampled(None, 1, ctypes.c_uint64(1), ctypes.c_float(t), None, None)
+        assert rc == -1, t  # KIE_ERR_INVALID_ARG
+        assert "temperature" in lib.kie_last_error().decode()
+    rc = lib.kie_decode_sampled(None, 1, ctypes.c_uint64(1), ctypes.c_float(0.7), None, None)
+    assert rc == -1  # KIE_ERR_INVALID_ARG
+    assert "handle" in lib.kie_last_error().decode()
