@@ -91,7 +91,8 @@ typedef enum kie_status {
                                  KIE_ERR_TIMEOUT instead of hanging. */
 
 typedef struct kie_config {
-  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_hidden;
+  int32_t n_layers;          /* 1..2048                                        */
+  int32_t d_model, n_heads, n_kv_heads, head_dim, ffn_hidden;
   int32_t vocab_in;          /* embedding rows                                 */
   int32_t vocab_out;         /* lm_head rows; must be <= vocab_in              */
   int32_t max_seq;           /* KV capacity in positions                       */

@@ -312,17 +312,19 @@ struct GemvWork {
   int rb;        // rows per block
 };
 
-__device__ __forceinline__ GemvWork gemv_work(int rows, int cols, int parts, int part, bool pairs) {
+// Rows are dealt out in units of `unit` consecutive rows (rows % unit == 0),
+// and row blocks hold whole units, so an epilogue can publish a unit's
+// results together (gate and up rows of one output, or pair words).
+__device__ __forceinline__ GemvWork gemv_work(int rows, int cols, int parts, int part, int unit) {
   GemvWork g;
   int b, e;
-  even_range(rows, parts, part, b, e);
-  g.r0 = b;
-  g.r1 = e;
+  even_range(rows / unit, parts, part, b, e);
+  g.r0 = b * unit;
+  g.r1 = e * unit;
   g.nch = cols >> 3;
   g.ks = (g.nch + 63) >> 6;
-  int rb = kPartCap / g.ks;
-  if (pairs) rb &= ~1;
-  g.rb = rb < 1 ? 1 : rb;
+  const int rb = (kPartCap / g.ks / unit) * unit;
+  g.rb = rb < unit ? unit : rb;
   return g;
 }
 
@@ -457,8 +459,16 @@ __device__ __forceinline__ void gemv_run(const GemvWork& g, const Addr& addr, co
 //
 // Every activation one workgroup hands to others (x, q/k/v, attention
 // partials, o, the FFN hidden u, router logits) lives in one arena of 64-bit
-// words: the low half is the fp32 value, the high half the epoch of the
-// stage that wrote it.  A producer writes each word with one device-scope
+// words holding a payload and the epoch of the stage that wrote it.  A
+// plain word is (epoch << 32) | fp32 bits.  The vectors that every
+// workgroup reads back in full as a GEMV input (x, o and u) travel as pair
+// words instead: two values, each the top 24 bits of its fp32 pattern
+// rounded to nearest even (sign, exponent and a 16-bit significand, relative
+// error at most 2^-16), in bits [0, 24) and [24, 48), and a 16-bit tag of
+// the epoch in bits [48, 64).  The cost of a gather follows the words each
+// of the 256 workgroups reads, so pairs halve it.  All arithmetic stays
+// fp32, and the residual stream also keeps plain words, which its owners,
+// the router and lm_head read.  A producer writes each word with one device-scope
 // 64-bit store (single-copy atomic), so a consumer that reads a word with
 // the epoch it expects also has the value: one load both synchronises and
 // delivers, and stages need no grid barrier and no store-completion wait.
@@ -489,6 +499,30 @@ __device__ __forceinline__ void ll_put(const Params& p, int word, float v, unsig
   __hip_atomic_store(p.act + word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The 16-bit tag of an epoch in a pair word: never 0, so a cleared word
+// never matches.  Two epochs share a tag only when they are a multiple of
+// 65535 apart.  A stale word is never that old when it is polled: within a
+// launch every pair word is rewritten once per layer (8 epochs), and a
+// launch's first wait on a word comes at most 16 * L + 16 epochs after that
+// word's last write in the previous launch (the host hands each launch
+// (steps + 1) * L * 8 + 8 epochs); n_layers <= 2048 keeps that below 65535.
+__device__ __forceinline__ unsigned pair_tag(unsigned flag) { return flag % 65535u + 1u; }
+
+// Top 24 bits of an fp32 pattern, rounded to nearest even.
+__device__ __forceinline__ unsigned f32_to_24(float v) {
+  const unsigned b = __float_as_uint(v);
+  return (b + 0x7Fu + ((b >> 8) & 1u)) >> 8;
+}
+
+// Two values in one pair word: a is element 2j, b element 2j + 1.
+__device__ __forceinline__ void ll_put2(const Params& p, int word, float a, float b, unsigned flag) {
+  const unsigned ua = f32_to_24(a), ub = f32_to_24(b);
+  const unsigned lo = ua | (ub << 24);
+  const unsigned hi = (ub >> 8) | (pair_tag(flag) << 16);
+  const u64 w = ((u64)hi << 32) | (u64)lo;
+  __hip_atomic_store(p.act + word, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ Rsrc arena_rsrc(const Params& p) {
   return make_rsrc(p.act, (size_t)p.act_words * 8);
 }
@@ -502,8 +536,9 @@ typedef __attribute__((address_space(3))) float lds_float;
 struct LLRange {
   int src;            // first arena word
   int n;              // words
-  float* dst;         // LDS destination
+  float* dst;         // LDS destination (2n floats for pair words)
   unsigned want;      // expected epoch
+  int pk = 0;         // 1: pair words (2 values each)
 };
 
 // Control state shared by every bounded wait of a workgroup.
@@ -533,6 +568,7 @@ constexpr int kGatherPer = 8;    // words per thread per pass
 // expected epochs and LDS destinations, and which of them are still pending.
 struct GatherSlots {
   unsigned pending;
+  unsigned pk;                      // slots holding pair words
   unsigned off[kGatherPer];
   unsigned want[kGatherPer];
   lds_float* dst[kGatherPer];       // 32-bit LDS addresses
@@ -542,6 +578,7 @@ template <int NR>
 __device__ __forceinline__ GatherSlots gather_slots(const LLRange (&rg)[NR], int total, int seg) {
   GatherSlots S;
   S.pending = 0;
+  S.pk = 0;
 #pragma unroll
   for (int k = 0; k < kGatherPer; ++k) {
     int i = seg + (int)threadIdx.x + k * kThreads;
@@ -554,8 +591,9 @@ __device__ __forceinline__ GatherSlots gather_slots(const LLRange (&rg)[NR], int
       for (int r = 0; r < NR; ++r) {
         if (i >= 0 && i < rg[r].n) {
           S.off[k] = (unsigned)(rg[r].src + i) * 8u;
-          S.want[k] = rg[r].want;
-          S.dst[k] = (lds_float*)(rg[r].dst + i);
+          S.want[k] = rg[r].pk ? pair_tag(rg[r].want) : rg[r].want;
+          S.dst[k] = (lds_float*)(rg[r].dst + (rg[r].pk ? 2 * i : i));
+          S.pk |= (unsigned)(rg[r].pk != 0) << k;
         }
         i -= rg[r].n;
       }
@@ -572,8 +610,14 @@ __device__ __forceinline__ void gather_issue(Rsrc arena, const GatherSlots& S, u
 __device__ __forceinline__ void gather_take(GatherSlots& S, const u32x2 (&v)[kGatherPer]) {
 #pragma unroll
   for (int k = 0; k < kGatherPer; ++k) {
-    if (((S.pending >> k) & 1u) && v[k].y == S.want[k]) {
-      *S.dst[k] = __uint_as_float(v[k].x);
+    const bool pk = (S.pk >> k) & 1u;
+    if (((S.pending >> k) & 1u) && (pk ? v[k].y >> 16 : v[k].y) == S.want[k]) {
+      if (pk) {
+        S.dst[k][0] = __uint_as_float(v[k].x << 8);
+        S.dst[k][1] = __uint_as_float(((v[k].y & 0xFFFFu) << 16) | ((v[k].x >> 24) << 8));
+      } else {
+        *S.dst[k] = __uint_as_float(v[k].x);
+      }
       S.pending &= ~(1u << k);
     }
   }
@@ -613,10 +657,16 @@ __device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherS
 // `issue()` is called once, right after the first poll loads are issued and
 // before their results are used: loads it issues (the next weights) queue
 // behind the first poll instead of in front of it, so that poll returns at
-// the fabric's latency rather than after the prefetch has landed (loads
-// return in issue order).  The first round is written out on its own so the
-// compiler sees a single issue order there.  Returns false (uniformly) when
-// a wait passes the timeout or another workgroup reported an error.
+// the fabric's latency rather than after the prefetch has landed (a wave's
+// loads return in issue order).  The first round is written out on its own
+// so the compiler sees a single issue order there.  Returns false
+// (uniformly) when a wait passes the timeout or another workgroup reported
+// an error.
+//
+// Handing the polling and the prefetch to different waves of the workgroup
+// measured slower: the exchange got no faster (the polls still meet the
+// streaming traffic beyond the compute unit) and the polling waves started
+// their share of the rows late.
 template <int NR, class Issue>
 __device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c,
                                           Issue&& issue) {
@@ -642,6 +692,17 @@ __device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[N
 template <int NR>
 __device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c) {
   return ll_gather(p, rg, c, [] {});
+}
+
+// A gather that prefetches the next stage's weights (issue) and the small
+// loads needed right after it (early: the norm gains) behind its first poll.
+template <int NR, class Early, class Issue>
+__device__ __forceinline__ bool ll_gather_pf(const Params& p, const LLRange (&rg)[NR], const Ctl& c,
+                                             Early&& early, Issue&& issue) {
+  return ll_gather(p, rg, c, [&]() {
+    issue();
+    early();
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -831,7 +892,7 @@ __device__ __forceinline__ Rsrc mat_rsrc(const __half* w, int rows, int cols) {
 // previous layer's down projection.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ GemvWork qkv_work(const Params& p, int wg) {
-  return gemv_work(p.H * p.hd + 2 * p.nkv * p.hd, p.d, p.n_wg, wg, false);
+  return gemv_work(p.H * p.hd + 2 * p.nkv * p.hd, p.d, p.n_wg, wg, 1);
 }
 __device__ __forceinline__ QkvAddr qkv_addr(const Params& p, int l) {
   const LayerPtrs w = layer(p, l);
@@ -854,13 +915,14 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
   const __half* gain = layer(p, l).attn_norm;
   WPre pre;
   GainPre G;
-  auto issue = [&]() {
-    pre = gemv_prefetch(g, addr);
-    G = gain_prefetch(gain, p.d);
-  };
+  auto gains = [&]() { G = gain_prefetch(gain, p.d); };
+  auto weights = [&]() { pre = gemv_prefetch(g, addr); };
   // Layer 0 waits for the grid barrier or reads the embedding: prefetch
   // first.  Later layers prefetch behind the first poll of x.
-  if (l == 0) issue();
+  if (l == 0) {
+    weights();
+    gains();
+  }
   if (wait_first) {
     if (!grid_wait(gs, c.flag)) return false;
     tok = resolve();
@@ -871,8 +933,8 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
       for (int i = threadIdx.x; i < p.d; i += kThreads) s.h[i] = __half2float(emb_row[i]);
     }
   } else if (g.r0 < g.r1) {
-    const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l - 1, kSlotXDown)}};
-    if (!ll_gather(p, rg, c, issue)) return false;
+    const LLRange rg[1] = {{p.off_xh, p.d / 2, s.h, ll_flag(p, step, l - 1, kSlotXDown), 1}};
+    if (!ll_gather_pf(p, rg, c, gains, weights)) return false;
   }
   mark(tr);
   if (g.r0 >= g.r1) {
@@ -987,18 +1049,19 @@ template <int G>
 __device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, const float* parts) {
   const int hd = p.hd, S = p.splits, ws = hd + 2;
   const unsigned fo = ll_flag(p, step, l, kSlotO);
-  for (int t = threadIdx.x; t < G * hd; t += kThreads) {
-    const int h = t / hd, i = t % hd;
+  for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
+    const int h = (2 * t) / hd, i = (2 * t) % hd;
     float M = kNegBig;
     for (int s = 0; s < S; ++s) M = fmaxf(M, parts[(s * G + h) * ws + hd]);
-    float Ls = 0.f, A = 0.f;
+    float Ls = 0.f, A0 = 0.f, A1 = 0.f;
     for (int s = 0; s < S; ++s) {
       const float* st = parts + (s * G + h) * ws;
       const float sc = exp2f(st[hd] - M);
       Ls = fmaf(st[hd + 1], sc, Ls);
-      A = fmaf(st[i], sc, A);
+      A0 = fmaf(st[i], sc, A0);
+      A1 = fmaf(st[i + 1], sc, A1);
     }
-    ll_put(p, p.off_o + (g * G + h) * hd + i, A / Ls, fo);
+    ll_put2(p, p.off_o + ((g * G + h) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
   }
 }
 
@@ -1243,21 +1306,23 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
   // merge the waves in order: this split's partial (or o itself when S == 1)
   const unsigned fp = ll_flag(p, step, l, kSlotPart);
   const unsigned fo = ll_flag(p, step, l, kSlotO);
-  for (int t = threadIdx.x; t < G * hd; t += kThreads) {
-    const int h = t / hd, i = t % hd;
+  for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
+    const int h = (2 * t) / hd, i = (2 * t) % hd;
     float M = kNegBig;
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, a.wst[(w * G + h) * ws + hd]);
-    float Ls = 0.f, A = 0.f;
+    float Ls = 0.f, A0 = 0.f, A1 = 0.f;
     for (int w = 0; w < kWaves; ++w) {
       const float* st = a.wst + (w * G + h) * ws;
       const float sc = exp2f(st[hd] - M);
       Ls = fmaf(st[hd + 1], sc, Ls);
-      A = fmaf(st[i], sc, A);
+      A0 = fmaf(st[i], sc, A0);
+      A1 = fmaf(st[i + 1], sc, A1);
     }
     if (S == 1) {
-      ll_put(p, p.off_o + (g * G + h) * hd + i, A / Ls, fo);
+      ll_put2(p, p.off_o + ((g * G + h) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
     } else {
-      ll_put(p, part_word(p, g, G, sidx, h, i), A, fp);
+      ll_put(p, part_word(p, g, G, sidx, h, i), A0, fp);
+      ll_put(p, part_word(p, g, G, sidx, h, i + 1), A1, fp);
       if (i == 0) {
         ll_put(p, part_word(p, g, G, sidx, h, hd), M, fp);
         ll_put(p, part_word(p, g, G, sidx, h, hd + 1), Ls, fp);
@@ -1308,8 +1373,24 @@ __device__ __forceinline__ bool stage_merge(const Params& p, int step, int l, in
 // and down projections; it reads its own previous x rows from the arena
 // together with the stage input.
 // ---------------------------------------------------------------------------
+// Adds a block's row sums to the owned residual rows and publishes the new
+// x twice: as plain fp32 words (read back by the owner, the router and
+// lm_head) and as pair words (the GEMV input of the next stages).  Blocks
+// start at even rows and hold an even number of them.
+__device__ __forceinline__ void put_residual(const Params& p, int b0, int n, int r0, const float* xown,
+                                             const float* sums, unsigned f) {
+  for (int j = threadIdx.x; 2 * j < n; j += kThreads) {
+    const int r = b0 + 2 * j;
+    const float v0 = xown[r - r0] + sums[2 * j];
+    const float v1 = xown[r + 1 - r0] + sums[2 * j + 1];
+    ll_put(p, p.off_x + r, v0, f);
+    ll_put(p, p.off_x + r + 1, v1, f);
+    ll_put2(p, p.off_xh + (r >> 1), v0, v1, f);
+  }
+}
+
 __device__ __forceinline__ GemvWork o_work(const Params& p, int wg) {
-  return gemv_work(p.d, p.H * p.hd, p.n_wg, wg, false);
+  return gemv_work(p.d, p.H * p.hd, p.n_wg, wg, 2);
 }
 __device__ __forceinline__ RowAddr o_addr(const Params& p, int l) {
   return RowAddr{mat_rsrc(layer(p, l).wo, p.d, p.H * p.hd), p.H * p.hd};
@@ -1324,28 +1405,22 @@ __device__ __forceinline__ bool stage_oproj(const Params& p, int step, int l, co
   if (l == 0) {
     for (int i = threadIdx.x; i < nown; i += kThreads) s.xown[i] = __half2float(emb_row[g.r0 + i]);
   }
-  const LLRange rg[2] = {{p.off_o, qd, s.h, ll_flag(p, step, l, kSlotO)},
+  const LLRange rg[2] = {{p.off_o, qd / 2, s.h, ll_flag(p, step, l, kSlotO), 1},
                          {p.off_x + g.r0, l == 0 ? 0 : nown, s.xown,
                           l == 0 ? 0u : ll_flag(p, step, l - 1, kSlotXDown)}};
-  if (!ll_gather(p, rg, c, [&]() { pre = gemv_prefetch(g, addr); })) return false;
+  if (!ll_gather_pf(p, rg, c, [] {}, [&]() { pre = gemv_prefetch(g, addr); })) return false;
   mark(tr);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXO);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const int r = b0 + i;
-      ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
-    }
+    put_residual(p, b0, n, g.r0, s.xown, sums, f);
   });
   return true;
 }
 
 // Stage: RMSNorm + paired gate/up GEMV + SwiGLU (dense FFN).
 __device__ __forceinline__ GemvWork gu_work(const Params& p, int wg) {
-  GemvWork g = gemv_work(p.F, p.d, p.n_wg, wg, true);
-  g.r0 *= 2;
-  g.r1 *= 2;
-  return g;
+  return gemv_work(2 * p.F, p.d, p.n_wg, wg, 4);      // virtual rows: 2 outputs of u per unit
 }
 __device__ __forceinline__ PairAddr gu_addr(const Params& p, int l) {
   const LayerPtrs w = layer(p, l);
@@ -1363,26 +1438,26 @@ __device__ __forceinline__ bool stage_gateup(const Params& p, int step, int l, i
   const __half* gain = layer(p, l).ffn_norm;
   WPre pre;
   GainPre G;
-  const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c, [&]() {
-        pre = gemv_prefetch(g, addr);
-        G = gain_prefetch(gain, p.d);
-      }))
+  const LLRange rg[1] = {{p.off_xh, p.d / 2, s.h, ll_flag(p, step, l, kSlotXO), 1}};
+  if (!ll_gather_pf(p, rg, c, [&]() { G = gain_prefetch(gain, p.d); },
+                    [&]() { pre = gemv_prefetch(g, addr); }))
     return false;
   mark(tr);
   const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotU);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
-    for (int i = threadIdx.x; 2 * i < n; i += kThreads)
-      ll_put(p, p.off_u + (b0 >> 1) + i, silu(sums[2 * i] * inv) * (sums[2 * i + 1] * inv), f);
+    // virtual rows 4j .. 4j + 3 = (gate, up) of u[2j] and of u[2j + 1]
+    for (int j = threadIdx.x; 4 * j < n; j += kThreads)
+      ll_put2(p, p.off_u + (b0 >> 2) + j, silu(sums[4 * j] * inv) * (sums[4 * j + 1] * inv),
+              silu(sums[4 * j + 2] * inv) * (sums[4 * j + 3] * inv), f);
   });
   return true;
 }
 
 // Stage: down GEMV + residual (dense FFN).
 __device__ __forceinline__ GemvWork down_work(const Params& p, int wg) {
-  return gemv_work(p.d, p.F, p.n_wg, wg, false);
+  return gemv_work(p.d, p.F, p.n_wg, wg, 2);
 }
 __device__ __forceinline__ RowAddr down_addr(const Params& p, int l) {
   return RowAddr{mat_rsrc(layer(p, l).w_down, p.d, p.F), p.F};
@@ -1393,17 +1468,14 @@ __device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int
   const RowAddr addr = down_addr(p, l);
   WPre pre;
   const int nown = g.r1 - g.r0;
-  const LLRange rg[2] = {{p.off_u, p.F, s.h, ll_flag(p, step, l, kSlotU)},
+  const LLRange rg[2] = {{p.off_u, p.F / 2, s.h, ll_flag(p, step, l, kSlotU), 1},
                          {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c, [&]() { pre = gemv_prefetch(g, addr); })) return false;
+  if (!ll_gather_pf(p, rg, c, [] {}, [&]() { pre = gemv_prefetch(g, addr); })) return false;
   mark(tr);
   mark(tr);
   const unsigned f = ll_flag(p, step, l, kSlotXDown);
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const int r = b0 + i;
-      ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
-    }
+    put_residual(p, b0, n, g.r0, s.xown, sums, f);
   });
   return true;
 }
@@ -1414,7 +1486,7 @@ __device__ __forceinline__ bool stage_down(const Params& p, int step, int l, int
 // from them.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ GemvWork router_work(const Params& p, int wg) {
-  return gemv_work(p.E, p.d, p.n_wg, wg, false);
+  return gemv_work(p.E, p.d, p.n_wg, wg, 1);
 }
 __device__ __forceinline__ RowAddr router_addr(const Params& p, int l) {
   return RowAddr{mat_rsrc(layer(p, l).router, p.E, p.d), p.d};
@@ -1423,16 +1495,18 @@ __device__ __forceinline__ bool stage_router(const Params& p, int step, int l, i
                                              const Ctl& c, Tracer& tr) {
   const GemvWork g = router_work(p, wg);
   const RowAddr addr = router_addr(p, l);
-  const WPre pre = gemv_prefetch(g, addr);
   if (g.r0 >= g.r1) {
     mark(tr);
     mark(tr);
     return true;
   }
   const __half* gain = layer(p, l).ffn_norm;
-  const GainPre G = gain_prefetch(gain, p.d);
+  WPre pre;
+  GainPre G;
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c)) return false;
+  if (!ll_gather_pf(p, rg, c, [&]() { G = gain_prefetch(gain, p.d); },
+                    [&]() { pre = gemv_prefetch(g, addr); }))
+    return false;
   mark(tr);
   const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
   mark(tr);
@@ -1475,10 +1549,7 @@ __device__ __forceinline__ int* moe_ids(Lds s) { return reinterpret_cast<int*>(s
 __device__ __forceinline__ float* moe_wts(Lds s) { return s.red + kRedWtsOff; }
 
 __device__ __forceinline__ GemvWork moe_gu_work(const Params& p, int wg) {
-  GemvWork g = gemv_work((p.topk + p.nshared) * p.Fe, p.d, p.n_wg, wg, true);
-  g.r0 *= 2;
-  g.r1 *= 2;
-  return g;
+  return gemv_work(2 * (p.topk + p.nshared) * p.Fe, p.d, p.n_wg, wg, 4);
 }
 __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int l, int wg, Lds s,
                                                  const Ctl& c, Tracer& tr) {
@@ -1506,9 +1577,11 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
   const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
   const unsigned f = ll_flag(p, step, l, kSlotU);
   gemv_run<false>(g, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
-    for (int i = threadIdx.x; 2 * i < n; i += kThreads) {
-      const int ff = (b0 >> 1) + i;
-      ll_put(p, p.off_u + ff, wts[ff / Fe] * silu(sums[2 * i] * inv) * (sums[2 * i + 1] * inv), f);
+    for (int j = threadIdx.x; 4 * j < n; j += kThreads) {     // u[ff], u[ff + 1]
+      const int ff = (b0 >> 1) + 2 * j;
+      ll_put2(p, p.off_u + (ff >> 1),
+              wts[ff / Fe] * silu(sums[4 * j] * inv) * (sums[4 * j + 1] * inv),
+              wts[(ff + 1) / Fe] * silu(sums[4 * j + 2] * inv) * (sums[4 * j + 3] * inv), f);
     }
   });
   return true;
@@ -1517,7 +1590,7 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
 // Down projection of all active experts as one GEMV whose row r is the
 // concatenation of each active expert's down row r (segments of Fe).
 __device__ __forceinline__ GemvWork moe_down_work(const Params& p, int wg) {
-  return gemv_work(p.d, (p.topk + p.nshared) * p.Fe, p.n_wg, wg, false);
+  return gemv_work(p.d, (p.topk + p.nshared) * p.Fe, p.n_wg, wg, 2);
 }
 __device__ __forceinline__ MoeDownAddr moe_down_addr(const Params& p, int l, Lds s) {
   return MoeDownAddr{mat_rsrc(layer(p, l).e_down, (p.E + p.nshared) * p.d, p.Fe), moe_ids(s), p.Fe,
@@ -1529,13 +1602,15 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
                                                bool have_routing, const Ctl& c, Tracer& tr) {
   const GemvWork g = moe_down_work(p, wg);
   WPre pre = {};
-  if (have_routing) pre = gemv_prefetch(g, moe_down_addr(p, l, s));
   const int nown = g.r1 - g.r0;
   const int A = p.topk + p.nshared;
-  const LLRange rg[3] = {{p.off_u, A * p.Fe, s.h, ll_flag(p, step, l, kSlotU)},
+  const LLRange rg[3] = {{p.off_u, A * p.Fe / 2, s.h, ll_flag(p, step, l, kSlotU), 1},
                          {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)},
                          {p.off_router, have_routing ? 0 : p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
-  if (!ll_gather(p, rg, c)) return false;
+  const bool ok = have_routing
+                      ? ll_gather_pf(p, rg, c, [] {}, [&]() { pre = gemv_prefetch(g, moe_down_addr(p, l, s)); })
+                      : ll_gather(p, rg, c);
+  if (!ok) return false;
   mark(tr);
   if (!have_routing) {
     moe_routing(p, moe_ids(s), moe_wts(s), s.sums);
@@ -1548,10 +1623,7 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
   const unsigned f = ll_flag(p, step, l, kSlotXDown);
   gemv_run<true>(g, moe_down_addr(p, l, s), s.h, s.part, s.sums, pre,
                  [&](int b0, int n, const float* sums) {
-                   for (int i = threadIdx.x; i < n; i += kThreads) {
-                     const int r = b0 + i;
-                     ll_put(p, p.off_x + r, s.xown[r - g.r0] + sums[i], f);
-                   }
+                   put_residual(p, b0, n, g.r0, s.xown, sums, f);
                  });
   return true;
 }
@@ -1606,7 +1678,7 @@ __device__ __forceinline__ float sample_key(float v, float temperature, unsigned
 }
 
 __device__ __forceinline__ GemvWork lm_work(const Params& p, int wg) {
-  return gemv_work(p.Vout, p.d, p.n_wg, wg, false);
+  return gemv_work(p.Vout, p.d, p.n_wg, wg, 1);
 }
 __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, Lds s, const Ctl& c,
                                              Tracer& tr) {
@@ -1620,10 +1692,8 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
   WPre pre;
   GainPre G;
   const LLRange rg[1] = {{p.off_x, p.d, s.h, ll_flag(p, step, p.L - 1, kSlotXDown)}};
-  if (!ll_gather(p, rg, c, [&]() {
-        pre = gemv_prefetch(g, addr);
-        G = gain_prefetch(p.final_norm, p.d);
-      }))
+  if (!ll_gather_pf(p, rg, c, [&]() { G = gain_prefetch(p.final_norm, p.d); },
+                    [&]() { pre = gemv_prefetch(g, addr); }))
     return false;
   mark(tr);
   const float inv = rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
@@ -1838,7 +1908,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_kernel(const __half* w, cons
   float* sums = part + kPartCap;
   for (int i = threadIdx.x; i < cols; i += kThreads) h[i] = x[i];
   __syncthreads();
-  gemv_run<false>(gemv_work(rows, cols, n_wg, blockIdx.x, false), RowAddr{mat_rsrc(w, rows, cols), cols},
+  gemv_run<false>(gemv_work(rows, cols, n_wg, blockIdx.x, 1), RowAddr{mat_rsrc(w, rows, cols), cols},
                   h, part, sums, WPre{}, [&](int b0, int n, const float* sm) {
                     for (int i = threadIdx.x; i < n; i += kThreads) y[b0 + i] = sm[i];
                   });

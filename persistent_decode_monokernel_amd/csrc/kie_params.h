@@ -48,12 +48,15 @@ struct Params {
   __half* vc;                   // [L][nkv][cap][hd]
   const float* rope_cos;        // [cap][hd/2]
   const float* rope_sin;        // [cap][hd/2]
-  unsigned long long* act;      // activation arena: 64-bit words (epoch << 32 | fp32 bits)
+  unsigned long long* act;      // activation arena of 64-bit words: plain (epoch << 32 | fp32
+                                // bits) or pair (two 24-bit-rounded fp32 values + epoch tag)
   int act_words;
-  int off_x;                    // [d]            residual stream
-  int off_qkv;                  // [H*hd + 2*nkv*hd]
-  int off_o;                    // [H*hd]         attention output (head-major)
-  int off_u;                    // [max(F, (topk+nshared)*Fe)]  FFN hidden
+  int off_x;                    // [d]            residual stream, plain (read by its owners,
+                                //                the router and lm_head)
+  int off_xh;                   // [d/2]          residual stream, pairs (GEMV inputs)
+  int off_qkv;                  // [H*hd + 2*nkv*hd]  plain
+  int off_o;                    // [H*hd/2]       attention output (head-major), pairs
+  int off_u;                    // [max(F, (topk+nshared)*Fe)/2]  FFN hidden, pairs
   int off_router;               // [E]            router logits
   int off_part;                 // [nkv][splits][G][hd+2]  split-K partials (acc, m, l)
   unsigned epoch0;              // epoch of (step 0, layer 0, slot 0) of this launch

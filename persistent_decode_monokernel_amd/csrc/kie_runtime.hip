@@ -224,7 +224,7 @@ const char* kie_last_error(void) { return g_err.c_str(); }
 int kie_config_check(const kie_config* c) {
   g_err.clear();
   if (!c) return fail(KIE_ERR_INVALID_ARG, "config is NULL");
-  if (c->n_layers < 1 || c->n_layers > 4096) return fail(KIE_ERR_INVALID_ARG, "n_layers out of range");
+  if (c->n_layers < 1 || c->n_layers > 2048) return fail(KIE_ERR_INVALID_ARG, "n_layers out of range (1..2048)");
   if (!is_mult(c->d_model, 8) || c->d_model > 32768)
     return fail(KIE_ERR_INVALID_ARG, "d_model must be a positive multiple of 8, at most 32768");
   if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0)
@@ -364,9 +364,10 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
       off += (words + 1) & ~(size_t)1;     // keep regions 16-byte aligned
     };
     region(p.off_x, d);
+    region(p.off_xh, d / 2);
     region(p.off_qkv, qd + 2 * kd);
-    region(p.off_o, qd);
-    region(p.off_u, ucount);
+    region(p.off_o, qd / 2);
+    region(p.off_u, ucount / 2);
     region(p.off_router, std::max(1, c.n_experts));
     region(p.off_part, (size_t)c.n_heads * p.splits * (hd + 2));
     if (off * 8 >= 0xFFFFFF00ull) return bail(fail(KIE_ERR_UNSUPPORTED, "activation arena too large"));
