@@ -979,15 +979,28 @@ struct AttnUnit {
   bool has_new, active;
 };
 
+// Splits per KV head at position pos: one per kSplitPositions cached
+// positions (the depth of the cache prefetch, so a split's rows are all in
+// flight before its inputs arrive), at most p.splits (the grid divided by
+// the KV heads, which also sizes the partial buffers).  Fewer splits make
+// the merge cheaper: its workgroup gathers every split's partial, and at
+// short contexts a full grid of splits would hold a few positions each.
+constexpr int kSplitPositions = kAU * kAttnStride;
+__device__ __forceinline__ int attn_splits(const Params& p, int pos) {
+  const int s = (pos + kSplitPositions) / kSplitPositions;     // ceil((pos + 1) / kSplitPositions)
+  return s < p.splits ? s : p.splits;
+}
+
 __device__ __forceinline__ AttnUnit attn_unit_of(const Params& p, int pos, int unit) {
   AttnUnit u;
-  const int units = p.nkv * p.splits;
+  const int S = attn_splits(p, pos);
+  const int units = p.nkv * S;
   u.active = unit < units;
-  u.g = u.active ? unit / p.splits : 0;
-  u.sidx = u.active ? unit % p.splits : 0;
+  u.g = u.active ? unit / S : 0;
+  u.sidx = u.active ? unit % S : 0;
   const int n = pos + 1;
-  u.p0 = split_begin(u.sidx, n, p.splits);
-  const int p1 = split_begin(u.sidx + 1, n, p.splits);
+  u.p0 = split_begin(u.sidx, n, S);
+  const int p1 = split_begin(u.sidx + 1, n, S);
   u.has_new = (p1 == n);
   u.pend = u.has_new ? pos : p1;               // cached positions [p0, pend)
   return u;
@@ -1046,8 +1059,9 @@ __device__ __forceinline__ int part_word(const Params& p, int g, int G, int s, i
 // Merges the S partials of head group g (in LDS, [S][G][hd+2]) in split
 // order and publishes o.
 template <int G>
-__device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, const float* parts) {
-  const int hd = p.hd, S = p.splits, ws = hd + 2;
+__device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, int S,
+                                           const float* parts) {
+  const int hd = p.hd, ws = hd + 2;
   const unsigned fo = ll_flag(p, step, l, kSlotO);
   for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
     const int h = (2 * t) / hd, i = (2 * t) % hd;
@@ -1068,20 +1082,20 @@ __device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int
 // Gathers head group g's partials and merges them (split 0's workgroup in
 // the persistent kernel, or the merge kernel of the staged mode).
 template <int G>
-__device__ __forceinline__ bool attn_gather_merge(const Params& p, int step, int l, int g, float* lds,
-                                                  const Ctl& c) {
+__device__ __forceinline__ bool attn_gather_merge(const Params& p, int step, int l, int g, int S,
+                                                  float* lds, const Ctl& c) {
   const AttnLds a = attn_lds<G>(p, lds);
-  const LLRange rg[1] = {{part_word(p, g, G, 0, 0, 0), p.splits * G * (p.hd + 2), a.parts,
+  const LLRange rg[1] = {{part_word(p, g, G, 0, 0, 0), S * G * (p.hd + 2), a.parts,
                           ll_flag(p, step, l, kSlotPart)}};
   if (!ll_gather(p, rg, c)) return false;
-  attn_merge<G>(p, step, l, g, a.parts);
+  attn_merge<G>(p, step, l, g, S, a.parts);
   return true;
 }
 
 template <int G, bool kPre, bool kMerge>
 __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int pos, const AttnUnit& U,
                                           float* lds, KVPre pre, const Ctl& c, Tracer& tr) {
-  const int hd = p.hd, half = hd >> 1, S = p.splits;
+  const int hd = p.hd, half = hd >> 1, S = attn_splits(p, pos);
   const int qd = p.H * hd, kd = p.nkv * hd;
   const int g = U.g, sidx = U.sidx, p0 = U.p0, pend = U.pend;
   const bool has_new = U.has_new;
@@ -1331,7 +1345,7 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
   }
   if (kMerge && S > 1 && sidx == 0) {
     __syncthreads();
-    return attn_gather_merge<G>(p, step, l, g, lds, c);
+    return attn_gather_merge<G>(p, step, l, g, S, lds, c);
   }
   return true;
 }
@@ -1342,7 +1356,7 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
 template <int G, bool kMerge>
 __device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int pos, int wg, Lds s,
                                            const Ctl& c, Tracer& tr) {
-  const int units = p.nkv * p.splits;
+  const int units = p.nkv * attn_splits(p, pos);
   if (wg >= units) {
     mark(tr);
     mark(tr);
@@ -1363,9 +1377,11 @@ __device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int
 
 // Staged mode: merge kernel body (split 0 of each head group merges).
 template <int G>
-__device__ __forceinline__ bool stage_merge(const Params& p, int step, int l, int wg, Lds s, const Ctl& c) {
-  if (p.splits <= 1 || wg >= p.nkv) return true;
-  return attn_gather_merge<G>(p, step, l, wg, s.h, c);
+__device__ __forceinline__ bool stage_merge(const Params& p, int step, int l, int pos, int wg, Lds s,
+                                            const Ctl& c) {
+  const int S = attn_splits(p, pos);
+  if (S <= 1 || wg >= p.nkv) return true;
+  return attn_gather_merge<G>(p, step, l, wg, S, s.h, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -1868,9 +1884,9 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(Params p, int stage,
       break;
     case kSMerge:
       switch (p.H / p.nkv) {
-        case 1: (void)stage_merge<1>(p, step, l, wg, s, c); break;
-        case 2: (void)stage_merge<2>(p, step, l, wg, s, c); break;
-        default: (void)stage_merge<4>(p, step, l, wg, s, c); break;
+        case 1: (void)stage_merge<1>(p, step, l, pos, wg, s, c); break;
+        case 2: (void)stage_merge<2>(p, step, l, pos, wg, s, c); break;
+        default: (void)stage_merge<4>(p, step, l, pos, wg, s, c); break;
       }
       break;
     case kSO: (void)stage_oproj(p, step, l, emb, wg, s, c, none); break;
