@@ -963,8 +963,8 @@ __device__ __forceinline__ bool stage_qkv(const Params& p, int step, int l, int 
 // order.  The split containing the current position rotates the new key,
 // rounds K and V to fp16, appends them to the cache and uses the rounded
 // values.  With one split per head the unit writes o directly; otherwise
-// each split publishes its (acc, m, l) partial and split 0 of each head
-// merges all splits in split order into o.  Scores carry log2(e)/sqrt(hd)
+// each split publishes its (acc, m, l) partial and split h of each head
+// group merges query head h's partials in split order into o.  Scores carry log2(e)/sqrt(hd)
 // so exp2 is the softmax exponential.
 // ---------------------------------------------------------------------------
 constexpr int kAttnStride = kWaves * 4;     // positions per workgroup per step
@@ -1052,43 +1052,56 @@ __device__ __forceinline__ AttnLds attn_lds(const Params& p, float* lds) {
 }
 
 // Arena word of split s's partial for query head (g*G + h), element i.
+// The partials of one query head are contiguous: [H][splits][hd + 2].
 __device__ __forceinline__ int part_word(const Params& p, int g, int G, int s, int h, int i) {
-  return p.off_part + (((g * p.splits + s) * G + h) * (p.hd + 2)) + i;
+  return p.off_part + (((g * G + h) * p.splits + s) * (p.hd + 2)) + i;
 }
 
-// Merges the S partials of head group g (in LDS, [S][G][hd+2]) in split
-// order and publishes o.
+// Merges, in split order, the S partials of the query heads h0, h0 + hs, ...
+// (< G) of head group g (in LDS, [head][S][hd+2]) and publishes their o.
 template <int G>
-__device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, int S,
-                                           const float* parts) {
+__device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int g, int S, int h0,
+                                           int hs, const float* parts) {
   const int hd = p.hd, ws = hd + 2;
+  const int nh = (G - h0 + hs - 1) / hs;
   const unsigned fo = ll_flag(p, step, l, kSlotO);
-  for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
-    const int h = (2 * t) / hd, i = (2 * t) % hd;
+  for (int t = threadIdx.x; 2 * t < nh * hd; t += kThreads) {     // elements i, i + 1 of head j
+    const int j = (2 * t) / hd, i = (2 * t) % hd;
+    const float* hp = parts + j * S * ws;
     float M = kNegBig;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, parts[(s * G + h) * ws + hd]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, hp[s * ws + hd]);
     float Ls = 0.f, A0 = 0.f, A1 = 0.f;
     for (int s = 0; s < S; ++s) {
-      const float* st = parts + (s * G + h) * ws;
+      const float* st = hp + s * ws;
       const float sc = exp2f(st[hd] - M);
       Ls = fmaf(st[hd + 1], sc, Ls);
       A0 = fmaf(st[i], sc, A0);
       A1 = fmaf(st[i + 1], sc, A1);
     }
-    ll_put2(p, p.off_o + ((g * G + h) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
+    ll_put2(p, p.off_o + ((g * G + h0 + j * hs) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
   }
 }
 
-// Gathers head group g's partials and merges them (split 0's workgroup in
-// the persistent kernel, or the merge kernel of the staged mode).
+// Gathers the partials of query heads h0, h0 + hs, ... of head group g and
+// merges them.  In the persistent kernel split s merges the heads h with
+// h mod S == s, so a group's G heads are merged by up to G workgroups, each
+// reading only its heads' partials; the staged mode's merge kernel gives
+// every query head its own workgroup.
 template <int G>
 __device__ __forceinline__ bool attn_gather_merge(const Params& p, int step, int l, int g, int S,
-                                                  float* lds, const Ctl& c) {
+                                                  int h0, int hs, float* lds, const Ctl& c) {
   const AttnLds a = attn_lds<G>(p, lds);
-  const LLRange rg[1] = {{part_word(p, g, G, 0, 0, 0), S * G * (p.hd + 2), a.parts,
-                          ll_flag(p, step, l, kSlotPart)}};
+  const int ws = p.hd + 2;
+  const unsigned want = ll_flag(p, step, l, kSlotPart);
+  LLRange rg[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int h = h0 + j * hs;
+    const bool on = h < G;
+    rg[j] = LLRange{part_word(p, g, G, 0, on ? h : 0, 0), on ? S * ws : 0, a.parts + j * S * ws, want};
+  }
   if (!ll_gather(p, rg, c)) return false;
-  attn_merge<G>(p, step, l, g, S, a.parts);
+  attn_merge<G>(p, step, l, g, S, h0, hs, a.parts);
   return true;
 }
 
@@ -1343,9 +1356,9 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
       }
     }
   }
-  if (kMerge && S > 1 && sidx == 0) {
+  if (kMerge && S > 1 && sidx < G) {
     __syncthreads();
-    return attn_gather_merge<G>(p, step, l, g, S, lds, c);
+    return attn_gather_merge<G>(p, step, l, g, S, sidx, S, lds, c);
   }
   return true;
 }
@@ -1375,13 +1388,17 @@ __device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int
   return true;
 }
 
-// Staged mode: merge kernel body (split 0 of each head group merges).
+// Staged mode: merge kernel body (one workgroup per query head).
 template <int G>
 __device__ __forceinline__ bool stage_merge(const Params& p, int step, int l, int pos, int wg, Lds s,
                                             const Ctl& c) {
   const int S = attn_splits(p, pos);
-  if (S <= 1 || wg >= p.nkv) return true;
-  return attn_gather_merge<G>(p, step, l, wg, S, s.h, c);
+  if (S <= 1) return true;
+  for (int u = wg; u < p.H; u += p.n_wg) {
+    if (!attn_gather_merge<G>(p, step, l, u / G, S, u % G, G, s.h, c)) return false;
+    __syncthreads();
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
