@@ -293,6 +293,31 @@ def test_variant_decode_parity(torch, kie, key):
     eng.close()
 
 
+def test_gqa_merge_with_fewer_splits_than_heads(torch, kie):
+    """Grouped-query attention (4 query heads per KV head) at positions
+    199..298, where the context-sized split count is 2, then 3: fewer splits
+    than query heads, so one merging workgroup merges several heads (split s
+    takes heads s, s + S, ...).  The staged mode, whose merge kernel gives
+    every query head its own workgroup, must give the same bits."""
+    cfg = _model("longctx", n_layers=2, prompt_len=200, n_decode=100)
+    _say("gqa fewer splits than heads")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    n = cfg.n_decode
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n)
+    o, zo = _oracle_replay(cfg, weights_to_numpy(W), prompt, toks)
+    rep = compare_steps(z, toks, zo)
+    _say("gqa fewer splits", rep)
+    assert rep["pinned"] >= n // 2
+    P = len(prompt)
+    _check_kv(eng, o, (0, 1), [(0, 8), (P - 2, P - 1 + n)])
+    eng.close()
+    eg, tg, zg = _run_gpu(torch, kie, cfg, W, prompt, n, graph=True)
+    np.testing.assert_array_equal(tg, toks)
+    np.testing.assert_array_equal(zg, z)
+    eg.close()
+
+
 def test_longctx_8192_prompt_attention(torch, kie):
     """The long-context head layout (GQA 32 x 80 over 8 KV heads) with the
     full 8192-token prompt and the full cache capacity, so the split-K
