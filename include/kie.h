@@ -146,6 +146,21 @@ int kie_create(const kie_config *cfg, const kie_weights *w, void *hip_stream,
  * outside [0, vocab_in); KIE_ERR_CONTEXT_OVERFLOW if n_tokens > max_seq. */
 int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
+/* As kie_prefill (same arguments, state afterwards and errors), but the
+ * prompt's positions go through each layer together, in chunks of 512:
+ * the weight products become dense matrix products on the matrix cores
+ * (fp16 weights times activations split into fp16 hi + lo parts,
+ * accumulated in fp32, so an fp32 product up to rounding order), followed
+ * by causal attention over the cache.  The K/V rows written agree with
+ * kie_prefill's up to fp32 rounding order.  Dense models only, with
+ * d_model, n_heads * head_dim and ffn_hidden multiples of 32; otherwise
+ * KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace of about
+ * 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes for the call
+ * and frees it before returning.  The batched product of a prompt's
+ * positions is the step before the decode path (the pages' method is
+ * decode; this follows from "matrix cores only in prefill, if at all"). */
+int kie_prefill_batched(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
+
 /* Generates n_steps tokens in one launch.  out_tokens: device int32
  * [n_steps] (required when n_steps > 0).  out_logits: device fp32
  * [n_steps][vocab_out] or NULL.  n_steps == 0 is a no-op.
@@ -206,6 +221,13 @@ int kie_debug_expert_ids(const kie_handle *h, int32_t pos0, int32_t pos1, int32_
  * workgroups. */
 int kie_debug_gemv(const void *w, const float *x, float *y, int32_t rows, int32_t cols,
                    int32_t n_workgroups, void *hip_stream);
+
+/* c = a w^T (or c += a w^T with accumulate != 0) with the batched
+ * prefill's matrix-core product: w device fp16 [n][k] row-major, a device
+ * fp32 [m][k], c device fp32 [m][n]; k a positive multiple of 32.  Allocates
+ * and frees a 4 m k byte workspace.  Synchronous on `hip_stream`. */
+int kie_debug_gemm(const void *w, const float *a, float *c, int32_t m, int32_t n, int32_t k,
+                   int32_t accumulate, void *hip_stream);
 
 /* Grid-barrier stress test: n_rounds barriers over n_workgroups persistent
  * workgroups; each round every workgroup checks that all others reached the

@@ -5,7 +5,7 @@ run every decode step of an fp16 decoder-only transformer inside one
 persistent launch.  This package is its thin Python binding.
 """
 from ._lib import KieError, STATUS, declared_functions, load
-from .engine import Engine, config_check, debug_barrier, debug_gemv, debug_stream, make_config
+from .engine import Engine, config_check, debug_barrier, debug_gemm, debug_gemv, debug_stream, make_config
 
-__all__ = ["Engine", "KieError", "STATUS", "config_check", "debug_barrier", "debug_gemv", "debug_stream",
-           "declared_functions", "load", "make_config"]
+__all__ = ["Engine", "KieError", "STATUS", "config_check", "debug_barrier", "debug_gemm", "debug_gemv",
+           "debug_stream", "declared_functions", "load", "make_config"]

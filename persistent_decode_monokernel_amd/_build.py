@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkie.so")
-SOURCES = ["kie_kernels.hip", "kie_runtime.hip"]
+SOURCES = ["kie_kernels.hip", "kie_prefill.hip", "kie_runtime.hip"]
 ARCH = "gfx950"
 
 

@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_config_check": (ctypes.c_int, [P(Config)]),
         "kie_create": (ctypes.c_int, [P(Config), P(Weights), VP, P(VP)]),
         "kie_prefill": (ctypes.c_int, [VP, P(I32), I32]),
+        "kie_prefill_batched": (ctypes.c_int, [VP, P(I32), I32]),
         "kie_decode": (ctypes.c_int, [VP, I32, VP, VP]),
         "kie_decode_sampled": (ctypes.c_int, [VP, I32, ctypes.c_uint64, ctypes.c_float, VP, VP]),
         "kie_reset": (ctypes.c_int, [VP]),
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_debug_read_kv": (ctypes.c_int, [VP, I32, I32, I32, VP, VP]),
         "kie_debug_expert_ids": (ctypes.c_int, [VP, I32, I32, P(I32)]),
         "kie_debug_gemv": (ctypes.c_int, [VP, VP, VP, I32, I32, I32, VP]),
+        "kie_debug_gemm": (ctypes.c_int, [VP, VP, VP, I32, I32, I32, I32, VP]),
         "kie_debug_barrier": (ctypes.c_int, [I32, I32, I32, P(I32), P(ctypes.c_float), VP]),
         "kie_debug_read_trace": (ctypes.c_int, [VP, P(ctypes.c_uint64), I32, P(I32), P(I32)]),
         "kie_debug_stream": (ctypes.c_int, [VP, VP, ctypes.c_size_t, I32, I32, P(ctypes.c_float), VP]),

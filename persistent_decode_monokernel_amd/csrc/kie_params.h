@@ -96,6 +96,19 @@ hipError_t launch_barrier_test(unsigned* bar, unsigned* slots, int* violations, 
                                hipStream_t s);
 hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, unsigned* sink,
                          hipStream_t s);
+// Batched prefill (kie_prefill.hip)
+hipError_t launch_split(const float* x, int ldx, __half* hi, __half* lo, int M, int K, hipStream_t s);
+hipError_t launch_gemm(const __half* ahi, const __half* alo, int lda, const __half* w, int ldw, float* c,
+                       int ldc, int M, int N, int K, bool accumulate, hipStream_t s);
+hipError_t launch_embed(const __half* emb, const int* tok, int d, float* X, int T, hipStream_t s);
+hipError_t launch_rmsnorm_split(const float* X, const __half* gain, int d, float eps, __half* hi, __half* lo,
+                                int T, hipStream_t s);
+hipError_t launch_rope_kv(float* QKV, int ldq, int H, int nkv, int hd, int pos0, const float* cosT,
+                          const float* sinT, __half* kc, __half* vc, int cap, int T, hipStream_t s);
+hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, const __half* vc, int cap, int H,
+                               int nkv, int hd, int pos0, float* O, int T, hipStream_t s);
+hipError_t launch_swiglu_split(const float* G, const float* U, size_t n, __half* hi, __half* lo,
+                               hipStream_t s);
 
 // Dynamic LDS layout (in floats) shared by host and device:
 //   [0, hcap)               GEMV input vector (largest GEMV input length) or

@@ -88,6 +88,7 @@ struct kie_handle {
   long long ticks_per_ms = 100000;
   std::vector<void*> allocs;     // every hipMalloc of this handle
   kie::LayerPtrs* d_layers = nullptr;
+  std::vector<kie::LayerPtrs> layers;   // host copy of the layer weight pointers
   int* d_prompt = nullptr;
   kie::Params* d_params = nullptr;   // device copy of the launch's parameter block
   kie::Params call{};                // host source of that copy (outlives the async copy)
@@ -412,6 +413,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
       tab[cap * half + q * half + j] = (float)std::sin(a);
     }
   }
+  h->layers = lp;
   if (hipMemcpy(h->d_layers, lp.data(), sizeof(kie::LayerPtrs) * c.n_layers, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(rc_tab, tab.data(), sizeof(float) * tab.size(), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemset(p.state, 0, 4 * sizeof(int)) != hipSuccess ||
@@ -452,7 +454,124 @@ int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
 namespace {
 int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, bool sample,
                  float temperature, uint64_t seed);
+
+// Batched prefill of positions 0 .. n - 2 in chunks of kPrefillChunk positions.
+// Per chunk and layer: RMSNorm -> Q/K/V products -> RoPE + fp16 K/V rows into
+// the cache -> causal attention over the cache -> O product + residual ->
+// RMSNorm -> gate/up products -> SwiGLU -> down product + residual.
+constexpr int kPrefillChunk = 512;
+
+int prefill_batched(kie_handle* h, int n) {
+  const kie::Params& p = h->base;
+  const int T = kPrefillChunk;
+  const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = p.F, qkv = qd + 2 * kd;
+  const int wide = std::max(std::max(d, qd), F);
+  const size_t fbytes = sizeof(float) * (size_t)T * ((size_t)d + qkv + qd + 2 * (size_t)F);
+  const size_t hbytes = sizeof(__half) * (size_t)T * wide * 2;
+  void* ws = nullptr;
+  hipError_t e = hipMalloc(&ws, fbytes + hbytes);
+  if (e != hipSuccess)
+    return fail(KIE_ERR_HIP, std::string("prefill workspace hipMalloc failed: ") + hipGetErrorString(e));
+  float* X = static_cast<float*>(ws);
+  float* QKV = X + (size_t)T * d;
+  float* O = QKV + (size_t)T * qkv;
+  float* G = O + (size_t)T * qd;
+  float* U = G + (size_t)T * F;
+  __half* hi = reinterpret_cast<__half*>(U + (size_t)T * F);
+  __half* lo = hi + (size_t)T * wide;
+  hipStream_t s = h->stream;
+  const size_t layer_kv = (size_t)p.nkv * p.cap * p.hd;
+  int rc = KIE_OK;
+  auto ok = [&](hipError_t err) {
+    if (err != hipSuccess && rc == KIE_OK)
+      rc = fail(KIE_ERR_HIP, std::string("prefill launch failed: ") + hipGetErrorString(err));
+    return rc == KIE_OK;
+  };
+  for (int c0 = 0; c0 < n - 1 && rc == KIE_OK; c0 += T) {
+    const int Tn = std::min(T, n - 1 - c0);
+    if (!ok(kie::launch_embed(p.tok_emb, h->d_prompt + c0, d, X, Tn, s))) break;
+    for (int l = 0; l < p.L && rc == KIE_OK; ++l) {
+      const kie::LayerPtrs& w = h->layers[l];
+      __half* kc = p.kc + (size_t)l * layer_kv;
+      __half* vc = p.vc + (size_t)l * layer_kv;
+      ok(kie::launch_rmsnorm_split(X, w.attn_norm, d, p.eps, hi, lo, Tn, s)) &&
+          ok(kie::launch_gemm(hi, lo, d, w.wq, d, QKV, qkv, Tn, qd, d, false, s)) &&
+          ok(kie::launch_gemm(hi, lo, d, w.wk, d, QKV + qd, qkv, Tn, kd, d, false, s)) &&
+          ok(kie::launch_gemm(hi, lo, d, w.wv, d, QKV + qd + kd, qkv, Tn, kd, d, false, s)) &&
+          ok(kie::launch_rope_kv(QKV, qkv, p.H, p.nkv, p.hd, c0, p.rope_cos, p.rope_sin, kc, vc, p.cap, Tn, s)) &&
+          ok(kie::launch_attn_prefill(QKV, qkv, kc, vc, p.cap, p.H, p.nkv, p.hd, c0, O, Tn, s)) &&
+          ok(kie::launch_split(O, qd, hi, lo, Tn, qd, s)) &&
+          ok(kie::launch_gemm(hi, lo, qd, w.wo, qd, X, d, Tn, d, qd, true, s)) &&
+          ok(kie::launch_rmsnorm_split(X, w.ffn_norm, d, p.eps, hi, lo, Tn, s)) &&
+          ok(kie::launch_gemm(hi, lo, d, w.w_gate, d, G, F, Tn, F, d, false, s)) &&
+          ok(kie::launch_gemm(hi, lo, d, w.w_up, d, U, F, Tn, F, d, false, s)) &&
+          ok(kie::launch_swiglu_split(G, U, (size_t)Tn * F, hi, lo, s)) &&
+          ok(kie::launch_gemm(hi, lo, F, w.w_down, F, X, d, Tn, d, F, true, s));
+    }
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess && rc == KIE_OK)
+    rc = fail(KIE_ERR_HIP, std::string("prefill failed: ") + hipGetErrorString(e));
+  (void)hipFree(ws);
+  return rc;
+}
 }  // namespace
+
+int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
+  g_err.clear();
+  if (!h || !tokens) return fail(KIE_ERR_INVALID_ARG, "handle or tokens is NULL");
+  if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
+  if (h->pos != 0 || h->pending) return fail(KIE_ERR_BAD_STATE, "prefill needs a fresh or reset handle");
+  if (n < 1) return fail(KIE_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (n > h->cfg.max_seq) return fail(KIE_ERR_CONTEXT_OVERFLOW, "prompt longer than max_seq");
+  const kie::Params& p = h->base;
+  if (p.E != 0) return fail(KIE_ERR_UNSUPPORTED, "batched prefill covers dense models; use kie_prefill");
+  if (p.d % 32 != 0 || (p.H * p.hd) % 32 != 0 || p.F % 32 != 0)
+    return fail(KIE_ERR_UNSUPPORTED, "batched prefill needs d_model, n_heads*head_dim and ffn_hidden "
+                                     "to be multiples of 32; use kie_prefill");
+  for (int i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= h->cfg.vocab_in)
+      return fail(KIE_ERR_TOKEN_RANGE, "prompt token " + std::to_string(i) + " out of range");
+  KIE_HIP(hipMemcpyAsync(h->d_prompt, tokens, sizeof(int) * n, hipMemcpyHostToDevice, h->stream));
+  KIE_HIP(hipEventRecord(h->ev0, h->stream));
+  int rc = prefill_batched(h, n);
+  if (rc) {
+    h->broken = true;
+    return rc;
+  }
+  // the pending token, where the decode kernel reads it
+  KIE_HIP(hipMemcpyAsync(h->base.state, h->d_prompt + (n - 1), sizeof(int), hipMemcpyDeviceToDevice,
+                         h->stream));
+  KIE_HIP(hipEventRecord(h->ev1, h->stream));
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  KIE_HIP(hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  h->pos = n - 1;
+  h->pending = true;
+  return KIE_OK;
+}
+
+int kie_debug_gemm(const void* w, const float* a, float* c, int32_t m, int32_t n, int32_t k,
+                   int32_t accumulate, void* hip_stream) {
+  g_err.clear();
+  if (m < 1 || n < 1 || k < 32 || k % 32 != 0 || m > 65536 || n > 65536 || k > 65536)
+    return fail(KIE_ERR_INVALID_ARG, "need m, n >= 1 and k a positive multiple of 32 (all <= 65536)");
+  int rc;
+  if ((rc = check_device_range(w, (size_t)n * k * sizeof(__half), "w"))) return rc;
+  if ((rc = check_device_range(a, (size_t)m * k * sizeof(float), "a"))) return rc;
+  if ((rc = check_device_range(c, (size_t)m * n * sizeof(float), "c"))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* ws = nullptr;
+  KIE_HIP(hipMalloc(&ws, sizeof(__half) * (size_t)m * k * 2));
+  __half* hi = static_cast<__half*>(ws);
+  __half* lo = hi + (size_t)m * k;
+  hipError_t e = kie::launch_split(a, k, hi, lo, m, k, s);
+  if (e == hipSuccess)
+    e = kie::launch_gemm(hi, lo, k, static_cast<const __half*>(w), k, c, n, m, n, k, accumulate != 0, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(ws);
+  if (e != hipSuccess) return fail(KIE_ERR_HIP, std::string("gemm failed: ") + hipGetErrorString(e));
+  return KIE_OK;
+}
 
 int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits) {
   g_err.clear();

@@ -80,6 +80,12 @@ class Engine:
         check(self.lib.kie_prefill(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                    int(t.size)), "kie_prefill")
 
+    def prefill_batched(self, tokens: Sequence[int]) -> None:
+        """kie_prefill_batched: the prompt's positions through each layer together."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        check(self.lib.kie_prefill_batched(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                           int(t.size)), "kie_prefill_batched")
+
     def decode_into(self, n: int, out_tokens: Optional[torch.Tensor],
                     out_logits: Optional[torch.Tensor] = None) -> None:
         tp = out_tokens.data_ptr() if out_tokens is not None else None
@@ -176,6 +182,21 @@ def debug_gemv(w: torch.Tensor, x: torch.Tensor, n_workgroups: int = 0) -> torch
     check(lib.kie_debug_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), rows, cols, n_workgroups,
                              ctypes.c_void_p(s.cuda_stream)), "kie_debug_gemv")
     return y
+
+
+def debug_gemm(w: torch.Tensor, a: torch.Tensor, c: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """c = a w^T (c += a w^T when c is given) through the batched prefill's
+    matrix-core product (w fp16 [n][k], a fp32 [m][k])."""
+    lib = _lib.load()
+    n, k = w.shape
+    m = a.shape[0]
+    acc = c is not None
+    if c is None:
+        c = torch.empty(m, n, dtype=torch.float32, device=w.device)
+    s = torch.cuda.current_stream()
+    check(lib.kie_debug_gemm(w.data_ptr(), a.data_ptr(), c.data_ptr(), m, n, k, int(acc),
+                             ctypes.c_void_p(s.cuda_stream)), "kie_debug_gemm")
+    return c
 
 
 def debug_barrier(n_workgroups: int = 0, rounds: int = 1000, spin_limit: int = 0):
