@@ -219,10 +219,11 @@ def main(argv=None):
     if args.warmup:
         eng.decode(args.warmup, logits=False)
     toks = torch.empty(K, dtype=torch.int32, device=dev)
-    times, kernel_ms = [], []
+    times, kernel_ms, prefill_ms = [], [], []
     for _ in range(max(1, args.reps)):
         eng.reset()
         eng.prefill(prompt)
+        prefill_ms.append(eng.last_elapsed_ms())
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -238,6 +239,15 @@ def main(argv=None):
     tok_s = K / (ms / 1e3)
     nbytes = decode_bytes(cfg, P - 1, K)
     achieved = nbytes / (kms / 1e3) / 1e9
+    # the prompt through the batched (matrix-core) prefill instead: not part
+    # of the decode metric, reported beside the persistent kernel's prefill
+    batched_ms = None
+    if not cfg.n_experts and not args.graph:
+        eng.reset()
+        eng.prefill_batched(prompt)
+        eng.reset()
+        eng.prefill_batched(prompt)
+        batched_ms = eng.last_elapsed_ms()
     eng.close()
     trace = None
     if args.trace and not args.graph:
@@ -279,7 +289,10 @@ def main(argv=None):
                    "roofline_tok_s": HBM_PEAK_GBS * 1e9 / (nbytes / K),
                    "hbm_probe": probes,
                    "frac_of_read_probe": (achieved / probes["read_gbs"]) if probes else None,
-                   "trace": trace},
+                   "trace": trace,
+                   "prefill": {"positions": P - 1,
+                               "persistent_ms": sorted(prefill_ms)[len(prefill_ms) // 2],
+                               "batched_ms": batched_ms}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

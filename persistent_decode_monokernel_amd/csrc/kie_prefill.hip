@@ -190,55 +190,119 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
   }
 }
 
-// Causal attention of position pos0 + t, query head i (blockIdx.y), over
-// cached positions 0 .. pos0 + t of KV head i / (H / nkv): softmax of
-// q . k / sqrt(hd) with the running maximum, in tiles of kAttnTile cached
-// positions.  Thread d < hd accumulates output element d.
-constexpr int kAttnTile = 1024;
+// Causal attention over the cache for a chunk's positions, tiled so that
+// the K/V rows staged in LDS serve many query rows: a block takes R / G
+// consecutive positions of the chunk and the G query heads that share KV
+// head g (blockIdx.y), i.e. R rows (row r = position r / G, query head
+// g * G + r % G; R = 64, or 32 for head sizes above 64 so that the block's
+// LDS stays under 64 KiB), and walks the cached positions 0 .. (its last
+// position) in tiles of kAK.  Per tile: scores S = q . k / sqrt(hd) with the
+// causal mask, the running maximum and sum per row (online softmax), and
+// O = O * rescale + P V.  fp32 throughout; K/V are the fp16 cache rows.
+constexpr int kAK = 64;                       // cached positions per tile
+constexpr int kAAcc = 16;                     // accumulators per thread: R * hd / kPT <= 16
+
+__host__ __device__ inline int attn_prefill_rows(int hd) { return hd > 64 ? 32 : 64; }
+
+size_t attn_prefill_lds(int hd) {
+  const size_t R = (size_t)attn_prefill_rows(hd);
+  return sizeof(float) * (R * hd + R * (kAK + 1) + 3 * R) +
+         sizeof(__half) * ((size_t)kAK * (hd + 2) + (size_t)kAK * hd);
+}
+
 __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
                                                           const __half* __restrict__ kc,
                                                           const __half* __restrict__ vc, int cap, int H,
-                                                          int nkv, int hd, int pos0, float* __restrict__ O) {
-  __shared__ float qs[kMaxHeadDim];
-  __shared__ float sc[kAttnTile];
-  __shared__ float red[kPT];
-  const int t = blockIdx.x, i = blockIdx.y, pos = pos0 + t;
-  const int g = i / (H / nkv);
+                                                          int nkv, int hd, int pos0, int T, float* __restrict__ O) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int G = H / nkv, R = attn_prefill_rows(hd), QP = R / G;
+  const int ks = hd + 2;                     // K row stride in halves (odd in 32-bit words)
+  float* Qs = lds;                           // [R][hd], pre-scaled
+  float* S = Qs + (size_t)R * hd;            // [R][kAK + 1]
+  float* rm = S + (size_t)R * (kAK + 1);     // running maximum per row
+  float* rl = rm + R;                        // running sum per row
+  float* rs = rl + R;                        // this tile's rescale per row
+  __half* Ks = reinterpret_cast<__half*>(rs + R);   // [kAK][hd + 2]
+  __half* Vs = Ks + (size_t)kAK * ks;               // [kAK][hd]
+  const int t0 = blockIdx.x * QP, g = blockIdx.y;
+  const int tn = min(QP, T - t0);                   // positions of this block
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int d = threadIdx.x; d < hd; d += kPT) qs[d] = QKV[(size_t)t * ldq + i * hd + d] * scale;
-  __syncthreads();
+  for (int e = threadIdx.x; e < R * hd; e += kPT) {
+    const int r = e / hd, d = e - r * hd;
+    const int tq = r / G, h = g * G + r % G;
+    Qs[e] = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
+  }
+  for (int r = threadIdx.x; r < R; r += kPT) {
+    rm[r] = -3.0e38f;
+    rl[r] = 0.f;
+  }
+  float acc[kAAcc];
+#pragma unroll
+  for (int u = 0; u < kAAcc; ++u) acc[u] = 0.f;
+  const int nacc = (R * hd + kPT - 1) / kPT;
   const __half* K = kc + (size_t)g * cap * hd;
   const __half* V = vc + (size_t)g * cap * hd;
-  float M = -3.0e38f, L = 0.f, acc = 0.f;
-  for (int j0 = 0; j0 <= pos; j0 += kAttnTile) {
-    const int n = min(kAttnTile, pos + 1 - j0);
-    float tmax = -3.0e38f;
-    for (int jj = threadIdx.x; jj < n; jj += kPT) {
-      const __half* kr = K + (size_t)(j0 + jj) * hd;
-      float s = 0.f;
-      for (int d = 0; d < hd; ++d) s = fmaf(qs[d], __half2float(kr[d]), s);
-      sc[jj] = s;
-      tmax = fmaxf(tmax, s);
+  const int last = pos0 + t0 + tn - 1;              // this block's last position
+  __syncthreads();
+  for (int k0 = 0; k0 <= last; k0 += kAK) {
+    const int nk = min(kAK, last + 1 - k0);
+    for (int e = threadIdx.x; e < nk * hd; e += kPT) {
+      const int j = e / hd, d = e - j * hd;
+      Ks[j * ks + d] = K[(size_t)(k0 + j) * hd + d];
+      Vs[j * hd + d] = V[(size_t)(k0 + j) * hd + d];
     }
-    const float Mn = fmaxf(M, block_max(tmax, red));
-    float tsum = 0.f;
-    for (int jj = threadIdx.x; jj < n; jj += kPT) {
-      const float e = __expf(sc[jj] - Mn);
-      sc[jj] = e;
-      tsum += e;
+    __syncthreads();
+    // scores, masked past each row's position
+    for (int e = threadIdx.x; e < R * kAK; e += kPT) {
+      const int r = e / kAK, j = e - r * kAK;
+      const int pos = pos0 + t0 + r / G;
+      float sv = -3.0e38f;
+      if (j < nk && k0 + j <= pos && r / G < tn) {
+        const float* q = Qs + (size_t)r * hd;
+        const __half* kr = Ks + j * ks;
+        float a = 0.f;
+        for (int d = 0; d < hd; ++d) a = fmaf(q[d], __half2float(kr[d]), a);
+        sv = a;
+      }
+      S[r * (kAK + 1) + j] = sv;
     }
-    const float rescale = __expf(M - Mn);
-    L = L * rescale + block_sum(tsum, red);       // block_sum's barriers also publish sc[]
-    if ((int)threadIdx.x < hd) {
-      float a = acc * rescale;
-      const __half* vcol = V + (size_t)j0 * hd + threadIdx.x;
-      for (int jj = 0; jj < n; ++jj) a = fmaf(sc[jj], __half2float(vcol[(size_t)jj * hd]), a);
-      acc = a;
+    __syncthreads();
+    // online softmax: one thread per row
+    for (int r = threadIdx.x; r < R; r += kPT) {
+      float* sr = S + r * (kAK + 1);
+      float mx = rm[r];
+      for (int j = 0; j < kAK; ++j) mx = fmaxf(mx, sr[j]);
+      float sum = 0.f;
+      for (int j = 0; j < kAK; ++j) {
+        const float pj = sr[j] > -1.0e38f ? __expf(sr[j] - mx) : 0.f;
+        sr[j] = pj;
+        sum += pj;
+      }
+      const float f = __expf(rm[r] - mx);
+      rs[r] = f;
+      rl[r] = rl[r] * f + sum;
+      rm[r] = mx;
     }
-    M = Mn;
+    __syncthreads();
+    // O = O * rescale + P V
+    for (int u = 0; u < nacc; ++u) {
+      const int e = threadIdx.x + u * kPT;
+      if (e >= R * hd) break;
+      const int r = e / hd, d = e - r * hd;
+      const float* pr = S + r * (kAK + 1);
+      float a = acc[u] * rs[r];
+      for (int j = 0; j < nk; ++j) a = fmaf(pr[j], __half2float(Vs[j * hd + d]), a);
+      acc[u] = a;
+    }
     __syncthreads();
   }
-  if ((int)threadIdx.x < hd) O[(size_t)t * H * hd + i * hd + threadIdx.x] = acc / L;
+  for (int u = 0; u < nacc; ++u) {
+    const int e = threadIdx.x + u * kPT;
+    if (e >= R * hd) break;
+    const int r = e / hd, d = e - r * hd;
+    const int tq = r / G, h = g * G + r % G;
+    if (tq < tn) O[(size_t)(t0 + tq) * H * hd + h * hd + d] = acc[u] / rl[r];
+  }
 }
 
 // S = silu(G) * U, split into hi/lo fp16.
@@ -267,8 +331,10 @@ hipError_t launch_rope_kv(float* QKV, int ldq, int H, int nkv, int hd, int pos0,
 }
 hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, const __half* vc, int cap, int H,
                                int nkv, int hd, int pos0, float* O, int T, hipStream_t s) {
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(T, H), dim3(kPT), 0, s, QKV, ldq, kc, vc, cap, H, nkv, hd,
-                     pos0, O);
+  const size_t lds = attn_prefill_lds(hd);          // < 64 KiB for every head size <= 128
+  const int qp = attn_prefill_rows(hd) / (H / nkv);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3((T + qp - 1) / qp, nkv), dim3(kPT), lds, s, QKV, ldq, kc, vc,
+                     cap, H, nkv, hd, pos0, T, O);
   return hipGetLastError();
 }
 hipError_t launch_swiglu_split(const float* G, const float* U, size_t n, __half* hi, __half* lo,
