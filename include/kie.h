@@ -153,7 +153,8 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * accumulated in fp32, so an fp32 product up to rounding order), followed
  * by causal attention over the cache.  The K/V rows written agree with
  * kie_prefill's up to fp32 rounding order.  Dense models only, with
- * d_model, n_heads * head_dim and ffn_hidden multiples of 32; otherwise
+ * d_model, n_heads * head_dim and ffn_hidden multiples of 32 and head_dim
+ * a multiple of 16; otherwise
  * KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace of about
  * 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes for the call
  * and frees it before returning.  The batched product of a prompt's

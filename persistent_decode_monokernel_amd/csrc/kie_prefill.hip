@@ -196,18 +196,130 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
 // head g (blockIdx.y), i.e. R rows (row r = position r / G, query head
 // g * G + r % G; R = 64, or 32 for head sizes above 64 so that the block's
 // LDS stays under 64 KiB), and walks the cached positions 0 .. (its last
-// position) in tiles of kAK.  Per tile: scores S = q . k / sqrt(hd) with the
-// causal mask, the running maximum and sum per row (online softmax), and
-// O = O * rescale + P V.  fp32 throughout; K/V are the fp16 cache rows.
+// position) in tiles of kAK.  Each row belongs to TPR = 256 / R adjacent
+// threads of one wave: thread i of a row scores keys i, i + TPR, ... of the
+// tile in registers, the row's maximum and sum are reduced across the TPR
+// lanes (online softmax), and the thread accumulates output dimensions
+// [i * hd / TPR, (i + 1) * hd / TPR) of P V.  fp32 throughout; K/V are the
+// fp16 cache rows.  Needs hd % 16 == 0.
 constexpr int kAK = 64;                       // cached positions per tile
-constexpr int kAAcc = 16;                     // accumulators per thread: R * hd / kPT <= 16
+constexpr int kAReg = 16;                     // per-thread registers: keys (kAK / TPR) and dims (hd / TPR)
 
 __host__ __device__ inline int attn_prefill_rows(int hd) { return hd > 64 ? 32 : 64; }
 
 size_t attn_prefill_lds(int hd) {
   const size_t R = (size_t)attn_prefill_rows(hd);
-  return sizeof(float) * (R * hd + R * (kAK + 1) + 3 * R) +
+  return sizeof(float) * (R * (hd + 2) + R * (kAK + 1)) +
          sizeof(__half) * ((size_t)kAK * (hd + 2) + (size_t)kAK * hd);
+}
+
+template <int TPR>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int TPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int TPR>
+__device__ __forceinline__ void attn_prefill_body(const float* __restrict__ QKV, int ldq,
+                                                  const __half* __restrict__ kc, const __half* __restrict__ vc,
+                                                  int cap, int H, int nkv, int hd, int pos0, int T,
+                                                  float* __restrict__ O, float* lds) {
+  constexpr int R = kPT / TPR, KPT = kAK / TPR;
+  const int G = H / nkv, QP = R / G, DPT = hd / TPR;
+  const int qs = hd + 2;                     // Q row stride (floats), keeps 2-word reads conflict-free
+  const int ks = hd + 2;                     // K row stride (halves), odd in 32-bit words
+  float* Qs = lds;                           // [R][hd + 2], pre-scaled
+  float* Pm = Qs + (size_t)R * qs;           // [R][kAK + 1] probabilities of the tile
+  __half* Ks = reinterpret_cast<__half*>(Pm + (size_t)R * (kAK + 1));   // [kAK][hd + 2]
+  __half* Vs = Ks + (size_t)kAK * ks;                                     // [kAK][hd]
+  const int t0 = blockIdx.x * QP, g = blockIdx.y;
+  const int tn = min(QP, T - t0);
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int e = threadIdx.x; e < R * hd; e += kPT) {
+    const int r = e / hd, d = e - r * hd;
+    const int tq = r / G, h = g * G + r % G;
+    Qs[r * qs + d] = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
+  }
+  const int r = threadIdx.x / TPR, i = threadIdx.x - r * TPR;
+  const int tq = r / G, pos = pos0 + t0 + tq;
+  const bool valid = tq < tn;
+  float m = -3.0e38f, l = 0.f, acc[kAReg];
+#pragma unroll
+  for (int k = 0; k < kAReg; ++k) acc[k] = 0.f;
+  const __half* K = kc + (size_t)g * cap * hd;
+  const __half* V = vc + (size_t)g * cap * hd;
+  const int last = pos0 + t0 + tn - 1;
+  const float* qr = Qs + r * qs;
+  float* pr = Pm + r * (kAK + 1);
+  __syncthreads();
+  for (int k0 = 0; k0 <= last; k0 += kAK) {
+    const int nk = min(kAK, last + 1 - k0);
+    for (int e = threadIdx.x; e < nk * (hd >> 1); e += kPT) {          // 2 halves at a time
+      const int j = e / (hd >> 1), d = 2 * (e - j * (hd >> 1));
+      *reinterpret_cast<__half2*>(&Ks[j * ks + d]) = *reinterpret_cast<const __half2*>(&K[(size_t)(k0 + j) * hd + d]);
+      *reinterpret_cast<__half2*>(&Vs[j * hd + d]) = *reinterpret_cast<const __half2*>(&V[(size_t)(k0 + j) * hd + d]);
+    }
+    __syncthreads();
+    float sc[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) sc[k] = 0.f;
+    for (int d = 0; d < hd; d += 2) {
+      const float2 q2 = *reinterpret_cast<const float2*>(qr + d);
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const float2 k2 = __half22float2(*reinterpret_cast<const __half2*>(&Ks[(i + TPR * k) * ks + d]));
+        sc[k] = fmaf(q2.x, k2.x, fmaf(q2.y, k2.y, sc[k]));
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = i + TPR * k;
+      if (!valid || j >= nk || k0 + j > pos) sc[k] = -3.0e38f;
+      mx = fmaxf(mx, sc[k]);
+    }
+    mx = group_max<TPR>(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const float pk = sc[k] > -1.0e38f ? __expf(sc[k] - mx) : 0.f;
+      pr[i + TPR * k] = pk;
+      sum += pk;
+    }
+    sum = group_sum<TPR>(sum);
+    const float f = __expf(m - mx);
+    l = l * f + sum;
+    m = mx;
+    __syncthreads();                         // the row's probabilities are in LDS
+    const int d0 = i * DPT;
+#pragma unroll
+    for (int k = 0; k < kAReg; ++k) acc[k] *= f;
+    for (int j = 0; j < nk; ++j) {
+      const float pj = pr[j];
+      const __half* vr = Vs + j * hd + d0;
+#pragma unroll
+      for (int k = 0; k < kAReg; k += 2) {
+        if (k < DPT) {
+          const float2 v2 = __half22float2(*reinterpret_cast<const __half2*>(vr + k));
+          acc[k] = fmaf(pj, v2.x, acc[k]);
+          acc[k + 1] = fmaf(pj, v2.y, acc[k + 1]);
+        }
+      }
+    }
+    __syncthreads();                         // before the next tile overwrites K, V and P
+  }
+  if (valid) {
+    const int h = g * G + r % G;
+    float* out = O + (size_t)(t0 + tq) * H * hd + h * hd + i * DPT;
+    for (int k = 0; k < DPT; ++k) out[k] = acc[k] / l;
+  }
 }
 
 __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
@@ -215,94 +327,10 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
                                                           const __half* __restrict__ vc, int cap, int H,
                                                           int nkv, int hd, int pos0, int T, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int G = H / nkv, R = attn_prefill_rows(hd), QP = R / G;
-  const int ks = hd + 2;                     // K row stride in halves (odd in 32-bit words)
-  float* Qs = lds;                           // [R][hd], pre-scaled
-  float* S = Qs + (size_t)R * hd;            // [R][kAK + 1]
-  float* rm = S + (size_t)R * (kAK + 1);     // running maximum per row
-  float* rl = rm + R;                        // running sum per row
-  float* rs = rl + R;                        // this tile's rescale per row
-  __half* Ks = reinterpret_cast<__half*>(rs + R);   // [kAK][hd + 2]
-  __half* Vs = Ks + (size_t)kAK * ks;               // [kAK][hd]
-  const int t0 = blockIdx.x * QP, g = blockIdx.y;
-  const int tn = min(QP, T - t0);                   // positions of this block
-  const float scale = 1.0f / sqrtf((float)hd);
-  for (int e = threadIdx.x; e < R * hd; e += kPT) {
-    const int r = e / hd, d = e - r * hd;
-    const int tq = r / G, h = g * G + r % G;
-    Qs[e] = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
-  }
-  for (int r = threadIdx.x; r < R; r += kPT) {
-    rm[r] = -3.0e38f;
-    rl[r] = 0.f;
-  }
-  float acc[kAAcc];
-#pragma unroll
-  for (int u = 0; u < kAAcc; ++u) acc[u] = 0.f;
-  const int nacc = (R * hd + kPT - 1) / kPT;
-  const __half* K = kc + (size_t)g * cap * hd;
-  const __half* V = vc + (size_t)g * cap * hd;
-  const int last = pos0 + t0 + tn - 1;              // this block's last position
-  __syncthreads();
-  for (int k0 = 0; k0 <= last; k0 += kAK) {
-    const int nk = min(kAK, last + 1 - k0);
-    for (int e = threadIdx.x; e < nk * hd; e += kPT) {
-      const int j = e / hd, d = e - j * hd;
-      Ks[j * ks + d] = K[(size_t)(k0 + j) * hd + d];
-      Vs[j * hd + d] = V[(size_t)(k0 + j) * hd + d];
-    }
-    __syncthreads();
-    // scores, masked past each row's position
-    for (int e = threadIdx.x; e < R * kAK; e += kPT) {
-      const int r = e / kAK, j = e - r * kAK;
-      const int pos = pos0 + t0 + r / G;
-      float sv = -3.0e38f;
-      if (j < nk && k0 + j <= pos && r / G < tn) {
-        const float* q = Qs + (size_t)r * hd;
-        const __half* kr = Ks + j * ks;
-        float a = 0.f;
-        for (int d = 0; d < hd; ++d) a = fmaf(q[d], __half2float(kr[d]), a);
-        sv = a;
-      }
-      S[r * (kAK + 1) + j] = sv;
-    }
-    __syncthreads();
-    // online softmax: one thread per row
-    for (int r = threadIdx.x; r < R; r += kPT) {
-      float* sr = S + r * (kAK + 1);
-      float mx = rm[r];
-      for (int j = 0; j < kAK; ++j) mx = fmaxf(mx, sr[j]);
-      float sum = 0.f;
-      for (int j = 0; j < kAK; ++j) {
-        const float pj = sr[j] > -1.0e38f ? __expf(sr[j] - mx) : 0.f;
-        sr[j] = pj;
-        sum += pj;
-      }
-      const float f = __expf(rm[r] - mx);
-      rs[r] = f;
-      rl[r] = rl[r] * f + sum;
-      rm[r] = mx;
-    }
-    __syncthreads();
-    // O = O * rescale + P V
-    for (int u = 0; u < nacc; ++u) {
-      const int e = threadIdx.x + u * kPT;
-      if (e >= R * hd) break;
-      const int r = e / hd, d = e - r * hd;
-      const float* pr = S + r * (kAK + 1);
-      float a = acc[u] * rs[r];
-      for (int j = 0; j < nk; ++j) a = fmaf(pr[j], __half2float(Vs[j * hd + d]), a);
-      acc[u] = a;
-    }
-    __syncthreads();
-  }
-  for (int u = 0; u < nacc; ++u) {
-    const int e = threadIdx.x + u * kPT;
-    if (e >= R * hd) break;
-    const int r = e / hd, d = e - r * hd;
-    const int tq = r / G, h = g * G + r % G;
-    if (tq < tn) O[(size_t)(t0 + tq) * H * hd + h * hd + d] = acc[u] / rl[r];
-  }
+  if (attn_prefill_rows(hd) == 32)
+    attn_prefill_body<8>(QKV, ldq, kc, vc, cap, H, nkv, hd, pos0, T, O, lds);
+  else
+    attn_prefill_body<4>(QKV, ldq, kc, vc, cap, H, nkv, hd, pos0, T, O, lds);
 }
 
 // S = silu(G) * U, split into hi/lo fp16.

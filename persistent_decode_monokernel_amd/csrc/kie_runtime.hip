@@ -526,9 +526,9 @@ int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
   if (n > h->cfg.max_seq) return fail(KIE_ERR_CONTEXT_OVERFLOW, "prompt longer than max_seq");
   const kie::Params& p = h->base;
   if (p.E != 0) return fail(KIE_ERR_UNSUPPORTED, "batched prefill covers dense models; use kie_prefill");
-  if (p.d % 32 != 0 || (p.H * p.hd) % 32 != 0 || p.F % 32 != 0)
+  if (p.d % 32 != 0 || (p.H * p.hd) % 32 != 0 || p.F % 32 != 0 || p.hd % 16 != 0)
     return fail(KIE_ERR_UNSUPPORTED, "batched prefill needs d_model, n_heads*head_dim and ffn_hidden "
-                                     "to be multiples of 32; use kie_prefill");
+                                     "to be multiples of 32 and head_dim of 16; use kie_prefill");
   for (int i = 0; i < n; ++i)
     if (tokens[i] < 0 || tokens[i] >= h->cfg.vocab_in)
       return fail(KIE_ERR_TOKEN_RANGE, "prompt token " + std::to_string(i) + " out of range");
