@@ -50,6 +50,7 @@ class ModelConfig:
     rms_eps: float = 1e-5
     rope_base: float = 10000.0
     max_seq: int = 0         # KV capacity; 0 -> prompt_len + n_decode
+    moe_renorm: bool = False # MoE: rescale the selected experts' probabilities to sum to 1
 
     @property
     def kv_capacity(self) -> int:

@@ -117,11 +117,13 @@ def moe_route(r: np.ndarray, top_k: int):
 
 
 def moe_ffn(h: np.ndarray, router: np.ndarray, expert, n_experts: int, top_k: int,
-            n_shared: int, router_log: Optional[list] = None) -> tuple:
+            n_shared: int, router_log: Optional[list] = None, renorm: bool = False) -> tuple:
     """Mixture-of-experts FFN for one token.
 
     y = sum over shared experts s of SwiGLU_s(h) + sum over the selected routed
-    experts e of pi_e * SwiGLU_e(h).  ``expert(e)`` returns the widened
+    experts e of w_e * SwiGLU_e(h), with w_e = pi_e, or, with ``renorm`` (the
+    other common reading of "softmax top-k"), w_e = pi_e / (sum of pi over the
+    selected experts), so that the routed weights sum to 1.  ``expert(e)`` returns the widened
     (gate, up, down) of expert e; ids n_experts.. are the shared experts.
     Only the experts used are touched (active-parameter streaming).
     Returns (y, selected ids); the router logits are appended to
@@ -130,13 +132,14 @@ def moe_ffn(h: np.ndarray, router: np.ndarray, expert, n_experts: int, top_k: in
     if router_log is not None:
         router_log.append(r)
     pi, sel = moe_route(r, top_k)
+    w = pi / pi[sel].sum() if renorm else pi
     y = np.zeros_like(h)
     for s in range(n_shared):
         g, u, d = expert(n_experts + s)
         y = y + swiglu(h, g, u, d)
     for e in sel:
         g, u, d = expert(int(e))
-        y = y + pi[e] * swiglu(h, g, u, d)
+        y = y + w[e] * swiglu(h, g, u, d)
     return y, sel
 
 
@@ -224,7 +227,8 @@ class Oracle:
         if not c.is_moe:
             return swiglu(h, self.lw(l, "w_gate"), self.lw(l, "w_up"), self.lw(l, "w_down")), None
         return moe_ffn(h, self.lw(l, "router"), lambda e: self.expert(l, e),
-                       c.n_experts, c.top_k, c.n_shared_experts, router_log)
+                       c.n_experts, c.top_k, c.n_shared_experts, router_log,
+                       renorm=getattr(c, "moe_renorm", False))
 
     # -- one token ----------------------------------------------------------
     def step(self, tok: int) -> np.ndarray:

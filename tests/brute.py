@@ -93,8 +93,9 @@ def last_logits(cfg, W, seq, return_experts=False):
                 for s_ in range(cfg.n_shared_experts):
                     k = cfg.n_experts + s_
                     y += _swiglu(h, lw["e_gate"][k], lw["e_up"][k], lw["e_down"][k])
+                tot = sum(pr[k] for k in sel) if getattr(cfg, "moe_renorm", False) else 1.0
                 for k in sel:
-                    y += pr[k] * _swiglu(h, lw["e_gate"][k], lw["e_up"][k], lw["e_down"][k])
+                    y += (pr[k] / tot) * _swiglu(h, lw["e_gate"][k], lw["e_up"][k], lw["e_down"][k])
                 if i == n - 1:
                     chosen.append(sel)
             else:

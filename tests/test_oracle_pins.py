@@ -194,6 +194,33 @@ def test_moe_single_expert_reduces_to_dense():
     assert list(sel) == [0]
 
 
+def test_moe_renormalised_weights_sum_to_one():
+    # every routed expert computes the same function f, so the routed part is
+    # (sum of the weights) * f: exactly f when renormalised, sum(pi_sel) * f otherwise
+    r = _rng(15)
+    d, F = 8, 6
+    h = r.normal(size=d)
+    same = (r.normal(size=(F, d)), r.normal(size=(F, d)), r.normal(size=(d, F)))
+    router = r.normal(size=(7, d))
+    f = swiglu(h, *same)
+    y, sel = moe_ffn(h, router, lambda e: same, 7, 3, 0, renorm=True)
+    np.testing.assert_allclose(y, f, rtol=1e-13)
+    pi, _ = moe_route(router @ h, 3)
+    y0, _ = moe_ffn(h, router, lambda e: same, 7, 3, 0)
+    np.testing.assert_allclose(y0, pi[sel].sum() * f, rtol=1e-13)
+
+
+def test_moe_renormalised_with_every_expert_selected_is_plain_softmax():
+    r = _rng(16)
+    d, F = 8, 5
+    h = r.normal(size=d)
+    ex = [(r.normal(size=(F, d)), r.normal(size=(F, d)), r.normal(size=(d, F))) for _ in range(5)]
+    router = r.normal(size=(4, d))
+    y1, _ = moe_ffn(h, router, lambda e: ex[e], 4, 4, 1, renorm=True)
+    y0, _ = moe_ffn(h, router, lambda e: ex[e], 4, 4, 1)
+    np.testing.assert_allclose(y1, y0, rtol=1e-12)
+
+
 def test_moe_shared_only():
     r = _rng(14)
     d, F = 8, 4
@@ -217,7 +244,10 @@ def _np_weights(cfg, seed=0, std=0.02):
     return weights_to_numpy(make_weights(cfg, seed=seed, std=std))
 
 
-@pytest.mark.parametrize("cfg", [SMALL, SMALL_GQA, SMALL_MOE], ids=lambda c: c.name)
+SMALL_MOE_RENORM = SMALL_MOE.with_(name="small_moe_renorm", moe_renorm=True)
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_GQA, SMALL_MOE, SMALL_MOE_RENORM], ids=lambda c: c.name)
 def test_decoder_matches_brute_force_recompute(cfg):
     # std 0.3 makes attention and routing far from uniform, so a wrong index
     # or sign shows up in the logits
