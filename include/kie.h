@@ -89,6 +89,12 @@ typedef enum kie_status {
                                  otherwise idle device; if it is not met, the
                                  barrier watchdog ends the call with
                                  KIE_ERR_TIMEOUT instead of hanging. */
+#define KIE_MOE_RENORM 0x10u  /* MoE models: the selected experts' softmax
+                                 probabilities are rescaled to sum to 1
+                                 before they weight the expert outputs
+                                 (default: used as they are).  The pages name
+                                 only "softmax top-k"; both readings are
+                                 offered. */
 
 typedef struct kie_config {
   int32_t n_layers;          /* 1..2048                                        */

@@ -18,6 +18,7 @@ STATUS = {
 KIE_MODE_GRAPH = 0x1
 KIE_TRACE = 0x2
 KIE_PLAIN_LAUNCH = 0x4
+KIE_MOE_RENORM = 0x10
 
 
 class KieError(RuntimeError):

@@ -1588,6 +1588,15 @@ __device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wt
     wts[K + a] = 1.0f;
   }
   __syncthreads();
+  if (p.moe_renorm) {
+    // the selected probabilities rescaled to sum to 1 (summed in rank order,
+    // the same in every workgroup)
+    float sel = 0.f;
+    for (int a = 0; a < K; ++a) sel += wts[a];
+    __syncthreads();
+    if ((int)threadIdx.x < K) wts[threadIdx.x] = wts[threadIdx.x] / sel;
+    __syncthreads();
+  }
 }
 
 __device__ __forceinline__ int* moe_ids(Lds s) { return reinterpret_cast<int*>(s.red + kRedIdsOff); }

@@ -35,6 +35,7 @@ struct Params {
   // ---- shapes
   int L, d, H, nkv, hd, F, Vin, Vout, cap;
   int E, topk, nshared, Fe;     // MoE (E == 0: dense)
+  int moe_renorm;               // MoE: routed weights rescaled to sum to 1
   float eps;
   int n_wg;                     // workgroups in the grid
   int splits;                   // attention position splits per KV head

@@ -69,6 +69,7 @@ kie::Params shape_params(const kie_config& c) {
   p.cap = c.max_seq;
   p.E = c.n_experts;
   p.topk = c.n_experts ? c.top_k : 0;
+  p.moe_renorm = (c.flags & KIE_MOE_RENORM) ? 1 : 0;
   p.nshared = c.n_experts ? c.n_shared_experts : 0;
   p.Fe = c.n_experts ? c.expert_hidden : 0;
   p.eps = c.rms_eps;
@@ -253,7 +254,7 @@ int kie_config_check(const kie_config* c) {
   if (c->max_seq < 1 || c->max_seq > (1 << 20)) return fail(KIE_ERR_INVALID_ARG, "max_seq out of range");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(KIE_ERR_INVALID_ARG, "rms_eps must be >= 0");
   if (!(c->rope_base > 1.f) || !std::isfinite(c->rope_base)) return fail(KIE_ERR_INVALID_ARG, "rope_base must be > 1");
-  if (c->flags & ~(KIE_MODE_GRAPH | KIE_TRACE | KIE_PLAIN_LAUNCH))
+  if (c->flags & ~(KIE_MODE_GRAPH | KIE_TRACE | KIE_PLAIN_LAUNCH | KIE_MOE_RENORM))
     return fail(KIE_ERR_INVALID_ARG, "unknown flag bits");
   if (c->n_workgroups < 0 || c->n_workgroups > 4096) return fail(KIE_ERR_INVALID_ARG, "n_workgroups out of range");
   if (c->timeout_ms < 0) return fail(KIE_ERR_INVALID_ARG, "timeout_ms < 0");

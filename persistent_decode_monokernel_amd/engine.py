@@ -28,7 +28,8 @@ def make_config(model, max_seq: Optional[int] = None, graph: bool = False,
         max_seq = getattr(model, "kv_capacity")
     c.max_seq = int(max_seq)
     c.flags = ((_lib.KIE_MODE_GRAPH if graph else 0) | (_lib.KIE_TRACE if trace else 0)
-               | (_lib.KIE_PLAIN_LAUNCH if plain_launch else 0))
+               | (_lib.KIE_PLAIN_LAUNCH if plain_launch else 0)
+               | (_lib.KIE_MOE_RENORM if getattr(model, "moe_renorm", False) else 0))
     c.n_workgroups = int(n_workgroups)
     c.timeout_ms = int(timeout_ms)
     return c
