@@ -190,27 +190,26 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
   }
 }
 
-// Causal attention over the cache for a chunk's positions, tiled so that
-// the K/V rows staged in LDS serve many query rows: a block takes R / G
-// consecutive positions of the chunk and the G query heads that share KV
-// head g (blockIdx.y), i.e. R rows (row r = position r / G, query head
-// g * G + r % G; R = 64, or 32 for head sizes above 64 so that the block's
-// LDS stays under 64 KiB), and walks the cached positions 0 .. (its last
-// position) in tiles of kAK.  Each row belongs to TPR = 256 / R adjacent
-// threads of one wave: thread i of a row scores keys i, i + TPR, ... of the
-// tile in registers, the row's maximum and sum are reduced across the TPR
-// lanes (online softmax), and the thread accumulates output dimensions
-// [i * hd / TPR, (i + 1) * hd / TPR) of P V.  fp32 throughout; K/V are the
-// fp16 cache rows.  Needs hd % 16 == 0.
-constexpr int kAK = 64;                       // cached positions per tile
-constexpr int kAReg = 16;                     // per-thread registers: keys (kAK / TPR) and dims (hd / TPR)
+// Causal attention over the cache for a chunk's positions, on the matrix
+// cores.  A block takes 32 rows: 32 / G consecutive positions of the chunk
+// times the G query heads that share KV head g (blockIdx.y); row r is
+// position r / G, query head g * G + r % G.  It walks the cached positions
+// 0 .. (its last position) in tiles of 32:
+//   S = Q K^T       one 32x32 MFMA tile (wave 0), Q split into fp16 hi + lo;
+//   online softmax  8 lanes per row: causal mask, running maximum and sum;
+//   O = O f + P V   wave w owns output columns [32 w, 32 w + 32), P split
+//                   into fp16 hi + lo, V staged transposed.
+// K and V are the fp16 cache rows (exact in fp16), so every product is an
+// fp32 product up to rounding order.  Needs hd % 16 == 0.
+constexpr int kMK = 32;                       // cached positions per tile (and rows per block)
 
-__host__ __device__ inline int attn_prefill_rows(int hd) { return hd > 64 ? 32 : 64; }
+__host__ __device__ inline int attn_qs(int hd) { return hd + 4; }   // padded row stride (halves)
+constexpr int kPS = kMK + 4;
 
 size_t attn_prefill_lds(int hd) {
-  const size_t R = (size_t)attn_prefill_rows(hd);
-  return sizeof(float) * (R * (hd + 2) + R * (kAK + 1)) +
-         sizeof(__half) * ((size_t)kAK * (hd + 2) + (size_t)kAK * hd);
+  const size_t hdp = (size_t)((hd + 31) & ~31);
+  const size_t halves = 3 * (size_t)kMK * attn_qs(hd) + hdp * kPS + 2 * (size_t)kMK * kPS;
+  return sizeof(_Float16) * halves + sizeof(float) * ((size_t)kMK * (kMK + 1) + 3 * kMK);
 }
 
 template <int TPR>
@@ -226,111 +225,135 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int TPR>
-__device__ __forceinline__ void attn_prefill_body(const float* __restrict__ QKV, int ldq,
-                                                  const __half* __restrict__ kc, const __half* __restrict__ vc,
-                                                  int cap, int H, int nkv, int hd, int pos0, int T,
-                                                  float* __restrict__ O, float* lds) {
-  constexpr int R = kPT / TPR, KPT = kAK / TPR;
-  const int G = H / nkv, QP = R / G, DPT = hd / TPR;
-  const int qs = hd + 2;                     // Q row stride (floats), keeps 2-word reads conflict-free
-  const int ks = hd + 2;                     // K row stride (halves), odd in 32-bit words
-  float* Qs = lds;                           // [R][hd + 2], pre-scaled
-  float* Pm = Qs + (size_t)R * qs;           // [R][kAK + 1] probabilities of the tile
-  __half* Ks = reinterpret_cast<__half*>(Pm + (size_t)R * (kAK + 1));   // [kAK][hd + 2]
-  __half* Vs = Ks + (size_t)kAK * ks;                                     // [kAK][hd]
-  const int t0 = blockIdx.x * QP, g = blockIdx.y;
-  const int tn = min(QP, T - t0);
-  const float scale = 1.0f / sqrtf((float)hd);
-  for (int e = threadIdx.x; e < R * hd; e += kPT) {
-    const int r = e / hd, d = e - r * hd;
-    const int tq = r / G, h = g * G + r % G;
-    Qs[r * qs + d] = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
-  }
-  const int r = threadIdx.x / TPR, i = threadIdx.x - r * TPR;
-  const int tq = r / G, pos = pos0 + t0 + tq;
-  const bool valid = tq < tn;
-  float m = -3.0e38f, l = 0.f, acc[kAReg];
-#pragma unroll
-  for (int k = 0; k < kAReg; ++k) acc[k] = 0.f;
-  const __half* K = kc + (size_t)g * cap * hd;
-  const __half* V = vc + (size_t)g * cap * hd;
-  const int last = pos0 + t0 + tn - 1;
-  const float* qr = Qs + r * qs;
-  float* pr = Pm + r * (kAK + 1);
-  __syncthreads();
-  for (int k0 = 0; k0 <= last; k0 += kAK) {
-    const int nk = min(kAK, last + 1 - k0);
-    for (int e = threadIdx.x; e < nk * (hd >> 1); e += kPT) {          // 2 halves at a time
-      const int j = e / (hd >> 1), d = 2 * (e - j * (hd >> 1));
-      *reinterpret_cast<__half2*>(&Ks[j * ks + d]) = *reinterpret_cast<const __half2*>(&K[(size_t)(k0 + j) * hd + d]);
-      *reinterpret_cast<__half2*>(&Vs[j * hd + d]) = *reinterpret_cast<const __half2*>(&V[(size_t)(k0 + j) * hd + d]);
-    }
-    __syncthreads();
-    float sc[KPT];
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) sc[k] = 0.f;
-    for (int d = 0; d < hd; d += 2) {
-      const float2 q2 = *reinterpret_cast<const float2*>(qr + d);
-#pragma unroll
-      for (int k = 0; k < KPT; ++k) {
-        const float2 k2 = __half22float2(*reinterpret_cast<const __half2*>(&Ks[(i + TPR * k) * ks + d]));
-        sc[k] = fmaf(q2.x, k2.x, fmaf(q2.y, k2.y, sc[k]));
-      }
-    }
-    float mx = m;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int j = i + TPR * k;
-      if (!valid || j >= nk || k0 + j > pos) sc[k] = -3.0e38f;
-      mx = fmaxf(mx, sc[k]);
-    }
-    mx = group_max<TPR>(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const float pk = sc[k] > -1.0e38f ? __expf(sc[k] - mx) : 0.f;
-      pr[i + TPR * k] = pk;
-      sum += pk;
-    }
-    sum = group_sum<TPR>(sum);
-    const float f = __expf(m - mx);
-    l = l * f + sum;
-    m = mx;
-    __syncthreads();                         // the row's probabilities are in LDS
-    const int d0 = i * DPT;
-#pragma unroll
-    for (int k = 0; k < kAReg; ++k) acc[k] *= f;
-    for (int j = 0; j < nk; ++j) {
-      const float pj = pr[j];
-      const __half* vr = Vs + j * hd + d0;
-#pragma unroll
-      for (int k = 0; k < kAReg; k += 2) {
-        if (k < DPT) {
-          const float2 v2 = __half22float2(*reinterpret_cast<const __half2*>(vr + k));
-          acc[k] = fmaf(pj, v2.x, acc[k]);
-          acc[k + 1] = fmaf(pj, v2.y, acc[k + 1]);
-        }
-      }
-    }
-    __syncthreads();                         // before the next tile overwrites K, V and P
-  }
-  if (valid) {
-    const int h = g * G + r % G;
-    float* out = O + (size_t)(t0 + tq) * H * hd + h * hd + i * DPT;
-    for (int k = 0; k < DPT; ++k) out[k] = acc[k] / l;
-  }
-}
-
 __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
                                                           const __half* __restrict__ kc,
                                                           const __half* __restrict__ vc, int cap, int H,
                                                           int nkv, int hd, int pos0, int T, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  if (attn_prefill_rows(hd) == 32)
-    attn_prefill_body<8>(QKV, ldq, kc, vc, cap, H, nkv, hd, pos0, T, O, lds);
-  else
-    attn_prefill_body<4>(QKV, ldq, kc, vc, cap, H, nkv, hd, pos0, T, O, lds);
+  const int G = H / nkv, QP = kMK / G, hdp = (hd + 31) & ~31, qs = attn_qs(hd);
+  _Float16* Qh = reinterpret_cast<_Float16*>(lds);     // [32][qs]
+  _Float16* Ql = Qh + kMK * qs;
+  _Float16* Ks = Ql + kMK * qs;                         // [32][qs]
+  _Float16* Vt = Ks + kMK * qs;                         // [hdp][kPS], V transposed
+  _Float16* Ph = Vt + hdp * kPS;                        // [32][kPS]
+  _Float16* Pl = Ph + kMK * kPS;
+  float* S = reinterpret_cast<float*>(Pl + kMK * kPS);  // [32][33]
+  float* rm = S + kMK * (kMK + 1);
+  float* rl = rm + kMK;
+  float* rf = rl + kMK;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * QP, g = blockIdx.y;
+  const int tn = min(QP, T - t0);
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int e = tid; e < kMK * hd; e += kPT) {
+    const int r = e / hd, d = e - r * hd;
+    const int tq = r / G, h = g * G + r % G;
+    const float v = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
+    const _Float16 hi = (_Float16)v;
+    Qh[r * qs + d] = hi;
+    Ql[r * qs + d] = (_Float16)(v - (float)hi);
+  }
+  for (int e = tid; e < (hdp - hd) * kPS; e += kPT) Vt[hd * kPS + e] = (_Float16)0.f;   // padded columns
+  if (tid < kMK) {
+    rm[tid] = -3.0e38f;
+    rl[tid] = 0.f;
+  }
+  f16acc acc = {};
+  const bool pv = wave * 32 < hdp;
+  const __half* K = kc + (size_t)g * cap * hd;
+  const __half* V = vc + (size_t)g * cap * hd;
+  const int last = pos0 + t0 + tn - 1;
+  const int kq0 = 4 * (lane >> 5), l32 = lane & 31;
+  // softmax lanes: row sr, lane si of its 8
+  const int sr = tid >> 3, si = tid & 7;
+  const int stq = sr / G, spos = pos0 + t0 + stq;
+  const bool svalid = stq < tn;
+  __syncthreads();
+  for (int k0 = 0; k0 <= last; k0 += kMK) {
+    const int nk = min(kMK, last + 1 - k0);
+    const int hd4 = hd >> 2;
+    for (int e = tid; e < kMK * hd4; e += kPT) {          // 4 halves (8 bytes) at a time
+      const int j = e / hd4, d = 4 * (e - j * hd4);
+      const bool in = j < nk;
+      const size_t src = (size_t)(k0 + (in ? j : 0)) * hd + d;
+      h4 kv = *reinterpret_cast<const h4*>(K + src);
+      h4 vv = *reinterpret_cast<const h4*>(V + src);
+      if (!in) {
+        kv = (h4){0, 0, 0, 0};
+        vv = (h4){0, 0, 0, 0};
+      }
+      *reinterpret_cast<h4*>(&Ks[j * qs + d]) = kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Vt[(d + i) * kPS + j] = vv[i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      f16acc sa = {};
+      for (int kk = 0; kk < hd; kk += 8) {
+        const h4 a_h = *reinterpret_cast<const h4*>(&Qh[l32 * qs + kk + kq0]);
+        const h4 a_l = *reinterpret_cast<const h4*>(&Ql[l32 * qs + kk + kq0]);
+        const h4 b = *reinterpret_cast<const h4*>(&Ks[l32 * qs + kk + kq0]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, sa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, sa, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) S[(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
+    }
+    __syncthreads();
+    {
+      float sc[4];
+      float mx = rm[sr];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = si + 8 * k;
+        float v = S[sr * (kMK + 1) + j];
+        if (!svalid || j >= nk || k0 + j > spos) v = -3.0e38f;
+        sc[k] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = group_max<8>(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float pk = sc[k] > -1.0e38f ? __expf(sc[k] - mx) : 0.f;
+        const _Float16 hi = (_Float16)pk;
+        Ph[sr * kPS + si + 8 * k] = hi;
+        Pl[sr * kPS + si + 8 * k] = (_Float16)(pk - (float)hi);
+        sum += pk;
+      }
+      sum = group_sum<8>(sum);
+      if (si == 0) {
+        const float f = __expf(rm[sr] - mx);
+        rf[sr] = f;
+        rl[sr] = rl[sr] * f + sum;
+        rm[sr] = mx;
+      }
+    }
+    __syncthreads();
+    if (pv) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] *= rf[8 * (j >> 2) + kq0 + (j & 3)];
+#pragma unroll
+      for (int kk = 0; kk < kMK; kk += 8) {
+        const h4 a_h = *reinterpret_cast<const h4*>(&Ph[l32 * kPS + kk + kq0]);
+        const h4 a_l = *reinterpret_cast<const h4*>(&Pl[l32 * kPS + kk + kq0]);
+        const h4 b = *reinterpret_cast<const h4*>(&Vt[(wave * 32 + l32) * kPS + kk + kq0]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (pv) {
+    const int d = wave * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + kq0 + (j & 3);
+      const int tq = r / G;
+      if (tq < tn && d < hd)
+        O[(size_t)(t0 + tq) * H * hd + (g * G + r % G) * hd + d] = acc[j] / rl[r];
+    }
+  }
 }
 
 // S = silu(G) * U, split into hi/lo fp16.
@@ -360,7 +383,7 @@ hipError_t launch_rope_kv(float* QKV, int ldq, int H, int nkv, int hd, int pos0,
 hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, const __half* vc, int cap, int H,
                                int nkv, int hd, int pos0, float* O, int T, hipStream_t s) {
   const size_t lds = attn_prefill_lds(hd);          // < 64 KiB for every head size <= 128
-  const int qp = attn_prefill_rows(hd) / (H / nkv);
+  const int qp = kMK / (H / nkv);
   hipLaunchKernelGGL(attn_prefill_kernel, dim3((T + qp - 1) / qp, nkv), dim3(kPT), lds, s, QKV, ldq, kc, vc,
                      cap, H, nkv, hd, pos0, T, O);
   return hipGetLastError();
