@@ -45,16 +45,28 @@ __global__ void split_kernel(const float* __restrict__ x, int ldx, __half* __res
 // C[M][N] (+)= (Ahi + Alo)[M][K] * W[N][K]^T with v_mfma_f32_32x32x8_f16.
 //
 // Block: 4 waves, a 64 x 64 tile of C; wave (wm, wn) owns a 32 x 32 quarter.
-// K advances 32 at a time through LDS (rows padded by 8 halves).  Operand
-// layout of the 32x32x8 MFMA: lane l holds A[l % 32][4 (l / 32) + i] and
-// B[4 (l / 32) + i][l % 32], i < 4, and accumulator j of lane l is
-// D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32].  B[k][n] is W[n][k], so both
-// operands are read as 4 consecutive halves of a row.
-// Requires K % 32 == 0 and 16-byte aligned rows (lda, ldw multiples of 8).
+// K advances kGK = 64 at a time through LDS (rows padded by 8 halves); the
+// next step's tiles are loaded into registers while the current step's
+// MFMAs run.  Operand layout of the 32x32x8 MFMA: lane l holds
+// A[l % 32][4 (l / 32) + i] and B[4 (l / 32) + i][l % 32], i < 4, and
+// accumulator j of lane l is D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32].
+// B[k][n] is W[n][k], so both operands are read as 4 consecutive halves of
+// a row.  Requires K % 32 == 0 and 16-byte aligned rows (lda, ldw multiples
+// of 8); a last step of 32 is zero-padded.
 // ---------------------------------------------------------------------------
 constexpr int kGT = 64;
-constexpr int kGK = 32;
+constexpr int kGK = 64;
 constexpr int kGPad = kGK + 8;
+
+// Raw buffer loads: an offset past the resource's size reads zeros, so the
+// ragged rows and the zero-padded last K step need no branches.
+constexpr unsigned kGOff = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(unsigned)bytes, (int)0x00020000u);
+}
+__device__ __forceinline__ uint4 gemm_ld(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ahi,
                                                    const __half* __restrict__ alo, int lda,
@@ -67,26 +79,43 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const int lr = tid >> 2, lc = (tid & 3) * 8;      // loader: row lr, 8 halves at column lc
+  // loader: row lr, 8 halves at columns lc and lc + 32 of each 64-wide step
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const __amdgpu_buffer_rsrc_t rh = gemm_rsrc(ahi, (size_t)M * lda * 2);
+  const __amdgpu_buffer_rsrc_t rl = gemm_rsrc(alo, (size_t)M * lda * 2);
+  const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(w, (size_t)N * ldw * 2);
   const bool am = m0 + lr < M, wnok = n0 + lr < N;
-  const __half* pa_h = ahi + (size_t)(am ? m0 + lr : 0) * lda + lc;
-  const __half* pa_l = alo + (size_t)(am ? m0 + lr : 0) * lda + lc;
-  const __half* pw = w + (size_t)(wnok ? n0 + lr : 0) * ldw + lc;
+  const unsigned abase = (unsigned)((m0 + lr) * lda + lc) * 2u;
+  const unsigned wbase = (unsigned)((n0 + lr) * ldw + lc) * 2u;
   f16acc acc = {};
   const int ar = (wm + (lane & 31)) * kGPad, br = (wn + (lane & 31)) * kGPad;
   const int kq0 = 4 * (lane >> 5);
+  uint4 h0, h1, l0, l1, w0, w1;
+  auto load = [&](int k0) {
+    const bool k1in = k0 + 32 < K;
+    const unsigned a0 = am ? abase + (unsigned)k0 * 2u : kGOff;
+    const unsigned a1 = (am && k1in) ? abase + (unsigned)(k0 + 32) * 2u : kGOff;
+    const unsigned b0 = wnok ? wbase + (unsigned)k0 * 2u : kGOff;
+    const unsigned b1 = (wnok && k1in) ? wbase + (unsigned)(k0 + 32) * 2u : kGOff;
+    h0 = gemm_ld(rh, a0);
+    h1 = gemm_ld(rh, a1);
+    l0 = gemm_ld(rl, a0);
+    l1 = gemm_ld(rl, a1);
+    w0 = gemm_ld(rw, b0);
+    w1 = gemm_ld(rw, b1);
+  };
+  load(0);
   for (int k0 = 0; k0 < K; k0 += kGK) {
-    uint4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-    if (am) {
-      vh = *reinterpret_cast<const uint4*>(pa_h + k0);
-      vl = *reinterpret_cast<const uint4*>(pa_l + k0);
-    }
-    if (wnok) vw = *reinterpret_cast<const uint4*>(pw + k0);
     __syncthreads();                                 // the previous step's reads are done
-    *reinterpret_cast<uint4*>(&sAh[lr * kGPad + lc]) = vh;
-    *reinterpret_cast<uint4*>(&sAl[lr * kGPad + lc]) = vl;
-    *reinterpret_cast<uint4*>(&sW[lr * kGPad + lc]) = vw;
+    const int o = lr * kGPad + lc;
+    *reinterpret_cast<uint4*>(&sAh[o]) = h0;
+    *reinterpret_cast<uint4*>(&sAh[o + 32]) = h1;
+    *reinterpret_cast<uint4*>(&sAl[o]) = l0;
+    *reinterpret_cast<uint4*>(&sAl[o + 32]) = l1;
+    *reinterpret_cast<uint4*>(&sW[o]) = w0;
+    *reinterpret_cast<uint4*>(&sW[o + 32]) = w1;
     __syncthreads();
+    if (k0 + kGK < K) load(k0 + kGK);                // in flight during the MFMAs
 #pragma unroll
     for (int kk = 0; kk < kGK; kk += 8) {
       const h4 a_h = *reinterpret_cast<const h4*>(&sAh[ar + kk + kq0]);
