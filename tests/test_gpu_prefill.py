@@ -116,6 +116,25 @@ def test_prefill_batched_agrees_with_persistent_prefill(torch, kie):
     b.close()
 
 
+def test_prefill_batched_then_staged_graph_decode(torch, kie):
+    """The staged (hipGraph) mode decodes from the state a batched prefill
+    leaves, and matches the persistent kernel decoding from it bit for bit."""
+    cfg = get_config("tiny")
+    W = make_weights(cfg, seed=0, device="cuda")
+    prompt = make_prompt(cfg)
+    a = kie.Engine(cfg, W)
+    a.prefill_batched(prompt)
+    ta, za = a.decode(24)
+    b = kie.Engine(cfg, W, graph=True)
+    b.prefill_batched(prompt)
+    tb, zb = b.decode(24)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ta.cpu().numpy(), tb.cpu().numpy())
+    np.testing.assert_array_equal(za.cpu().numpy(), zb.cpu().numpy())
+    a.close()
+    b.close()
+
+
 def test_prefill_batched_rejects_moe_and_bad_state(torch, kie):
     cfg = get_config("moe", n_layers=1, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, vocab_in=512,
                      vocab_out=512, n_experts=4, top_k=2, n_shared_experts=1, expert_hidden=64,
