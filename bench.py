@@ -242,7 +242,7 @@ def main(argv=None):
     # the prompt through the batched (matrix-core) prefill instead: not part
     # of the decode metric, reported beside the persistent kernel's prefill
     batched_ms = None
-    if not cfg.n_experts and not args.graph:
+    if not args.graph:
         eng.reset()
         eng.prefill_batched(prompt)
         eng.reset()

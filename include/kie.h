@@ -158,12 +158,14 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * (fp16 weights times activations split into fp16 hi + lo parts,
  * accumulated in fp32, so an fp32 product up to rounding order), followed
  * by causal attention over the cache.  The K/V rows written agree with
- * kie_prefill's up to fp32 rounding order.  Dense models only, with
- * d_model, n_heads * head_dim and ffn_hidden multiples of 32 and head_dim
- * a multiple of 16; otherwise
- * KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace of about
- * 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes for the call
- * and frees it before returning.  The batched product of a prompt's
+ * kie_prefill's up to fp32 rounding order.  MoE models route every
+ * position (the routing record of kie_debug_expert_ids is filled), group
+ * the positions by expert on the host and run each expert's products over
+ * its rows.  Needs d_model, n_heads * head_dim and ffn_hidden (MoE:
+ * expert_hidden) to be multiples of 32 and head_dim a multiple of 16;
+ * otherwise KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace
+ * (about 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes, more
+ * for MoE) for the call and frees it before returning.  The batched product of a prompt's
  * positions is the step before the decode path (the pages' method is
  * decode; this follows from "matrix cores only in prefill, if at all"). */
 int kie_prefill_batched(kie_handle *h, const int32_t *tokens, int32_t n_tokens);

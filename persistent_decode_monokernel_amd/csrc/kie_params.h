@@ -110,6 +110,13 @@ hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, cons
                                int nkv, int hd, int pos0, float* O, int T, hipStream_t s);
 hipError_t launch_swiglu_split(const float* G, const float* U, size_t n, __half* hi, __half* lo,
                                hipStream_t s);
+hipError_t launch_route(const float* R, int E, int topk, int renorm, int* ids, float* wts, int* log, int L, int l,
+                        int pos0, int T, hipStream_t s);
+hipError_t launch_gather_rows(const __half* hi, const __half* lo, int d, const int* perm, int topk, __half* ch,
+                              __half* cl, int rows, hipStream_t s);
+hipError_t launch_swiglu_w_split(const float* G, const float* U, int F, int rows, const int* perm, const float* wts,
+                                 __half* hi, __half* lo, hipStream_t s);
+hipError_t launch_combine(float* X, int d, const float* Y, const int* inv, int topk, int T, hipStream_t s);
 
 // Dynamic LDS layout (in floats) shared by host and device:
 //   [0, hcap)               GEMV input vector (largest GEMV input length) or

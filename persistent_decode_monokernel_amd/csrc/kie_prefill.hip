@@ -394,6 +394,110 @@ __global__ void swiglu_split_kernel(const float* __restrict__ G, const float* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Mixture-of-experts FFN over a chunk: routing per position, then the
+// positions grouped by expert (the host builds the grouping from the
+// routing) so each expert's products are dense products over its rows.
+// ---------------------------------------------------------------------------
+// Routing of position t from its router logits R[t][E]: softmax in fp32, the
+// top_k probabilities (lower id on ties) as ids[t][a] and weights wts[t][a]
+// in rank order (rescaled to sum to 1 with renorm); the ids also go to the
+// routing record by position.  One block per position.
+__global__ __launch_bounds__(kPT) void route_kernel(const float* __restrict__ R, int E, int topk, int renorm,
+                                                   int* __restrict__ ids, float* __restrict__ wts,
+                                                   int* __restrict__ log, int L, int l, int pos0) {
+  __shared__ float red[kPT];
+  __shared__ float sw[kMaxActiveExperts];
+  const int t = blockIdx.x;
+  const float* r = R + (size_t)t * E;
+  float mx = -3.0e38f;
+  for (int e = threadIdx.x; e < E; e += kPT) mx = fmaxf(mx, r[e]);
+  mx = block_max(mx, red);
+  float den = 0.f;
+  for (int e = threadIdx.x; e < E; e += kPT) den += __expf(r[e] - mx);
+  den = block_sum(den, red);
+  for (int e = threadIdx.x; e < E; e += kPT) {
+    const float re = r[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const float rj = r[j];
+      rank += (rj > re) || (rj == re && j < e);
+    }
+    if (rank < topk) {
+      ids[t * topk + rank] = e;
+      sw[rank] = __expf(re - mx) / den;
+      log[((size_t)(pos0 + t) * L + l) * topk + rank] = e;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < topk) {
+    float sel = 1.f;
+    if (renorm) {
+      sel = 0.f;
+      for (int a = 0; a < topk; ++a) sel += sw[a];
+    }
+    wts[t * topk + threadIdx.x] = sw[threadIdx.x] / sel;
+  }
+}
+
+// Compact row q takes position perm[q] / topk: its hi/lo input row.
+__global__ __launch_bounds__(kPT) void gather_rows_kernel(const __half* __restrict__ hi, const __half* __restrict__ lo,
+                                                         int d, const int* __restrict__ perm, int topk,
+                                                         __half* __restrict__ ch, __half* __restrict__ cl) {
+  const int q = blockIdx.x, t = perm[q] / topk;
+  for (int i = threadIdx.x; i < d; i += kPT) {
+    ch[(size_t)q * d + i] = hi[(size_t)t * d + i];
+    cl[(size_t)q * d + i] = lo[(size_t)t * d + i];
+  }
+}
+
+// S[q] = w[q] * silu(G[q]) * U[q] over rows q < rows, split into hi/lo; the
+// weight of compact row q is wts[perm[q]] (or 1 without perm).
+__global__ void swiglu_w_split_kernel(const float* __restrict__ G, const float* __restrict__ U, int F, int rows,
+                                      const int* __restrict__ perm, const float* __restrict__ wts,
+                                      __half* __restrict__ hi, __half* __restrict__ lo) {
+  const size_t n = (size_t)rows * F;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int q = (int)(i / F);
+    const float w = perm ? wts[perm[q]] : 1.f;
+    const float a = G[i];
+    split_store(w * (a / (1.0f + __expf(-a)) * U[i]), hi, lo, i);
+  }
+}
+
+// X[t] += sum over a < topk (rank order) of Y[inv[t * topk + a]].
+__global__ __launch_bounds__(kPT) void combine_kernel(float* __restrict__ X, int d, const float* __restrict__ Y,
+                                                     const int* __restrict__ inv, int topk) {
+  const int t = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += kPT) {
+    float v = 0.f;
+    for (int a = 0; a < topk; ++a) v += Y[(size_t)inv[t * topk + a] * d + i];
+    X[(size_t)t * d + i] += v;
+  }
+}
+
+hipError_t launch_route(const float* R, int E, int topk, int renorm, int* ids, float* wts, int* log, int L, int l,
+                        int pos0, int T, hipStream_t s) {
+  hipLaunchKernelGGL(route_kernel, dim3(T), dim3(kPT), 0, s, R, E, topk, renorm, ids, wts, log, L, l, pos0);
+  return hipGetLastError();
+}
+hipError_t launch_gather_rows(const __half* hi, const __half* lo, int d, const int* perm, int topk, __half* ch,
+                              __half* cl, int rows, hipStream_t s) {
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(kPT), 0, s, hi, lo, d, perm, topk, ch, cl);
+  return hipGetLastError();
+}
+hipError_t launch_swiglu_w_split(const float* G, const float* U, int F, int rows, const int* perm, const float* wts,
+                                 __half* hi, __half* lo, hipStream_t s) {
+  const size_t blocks = ((size_t)rows * F + 255) / 256;
+  const int grid = (int)(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(swiglu_w_split_kernel, dim3(grid), dim3(256), 0, s, G, U, F, rows, perm, wts, hi, lo);
+  return hipGetLastError();
+}
+hipError_t launch_combine(float* X, int d, const float* Y, const int* inv, int topk, int T, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kPT), 0, s, X, d, Y, inv, topk);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(const __half* emb, const int* tok, int d, float* X, int T, hipStream_t s) {
   hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(kPT), 0, s, emb, tok, d, X);
   return hipGetLastError();

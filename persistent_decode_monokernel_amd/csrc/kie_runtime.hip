@@ -462,17 +462,109 @@ int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logit
 // RMSNorm -> gate/up products -> SwiGLU -> down product + residual.
 constexpr int kPrefillChunk = 512;
 
+// Mixture-of-experts FFN of one chunk and layer (hi/lo hold the normed
+// input): router product, routing per position, positions grouped by expert
+// on the host, per-expert products over the grouped rows, shared experts over
+// all rows, and the weighted expert outputs summed back in rank order.
+struct MoeWs {
+  float *R, *wts, *Gc, *Uc, *Yc;
+  int *ids, *perm, *inv;
+  __half *ch, *cl, *sh, *sl;
+  std::vector<int> h_ids, h_perm, h_inv, off;
+};
+
+int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int Tn, const __half* hi,
+                    const __half* lo, float* X, MoeWs& m) {
+  const kie::Params& p = h->base;
+  hipStream_t s = h->stream;
+  const int d = p.d, E = p.E, k = p.topk, Fe = p.Fe, rows = Tn * k;
+  auto ok = [&](hipError_t err) {
+    return err == hipSuccess ? KIE_OK : fail(KIE_ERR_HIP, std::string("prefill launch failed: ") + hipGetErrorString(err));
+  };
+  int rc;
+  if ((rc = ok(kie::launch_gemm(hi, lo, d, w.router, d, m.R, E, Tn, E, d, false, s)))) return rc;
+  if ((rc = ok(kie::launch_route(m.R, E, k, p.moe_renorm, m.ids, m.wts, p.expert_log, p.L, l, c0, Tn, s)))) return rc;
+  KIE_HIP(hipMemcpyAsync(m.h_ids.data(), m.ids, sizeof(int) * rows, hipMemcpyDeviceToHost, s));
+  KIE_HIP(hipStreamSynchronize(s));
+  // compact rows ordered by expert, then position: perm[q] = t * k + a
+  std::fill(m.off.begin(), m.off.end(), 0);
+  for (int i = 0; i < rows; ++i) ++m.off[m.h_ids[i] + 1];
+  for (int e = 0; e < E; ++e) m.off[e + 1] += m.off[e];
+  std::vector<int> fill(m.off.begin(), m.off.end() - 1);
+  for (int i = 0; i < rows; ++i) {
+    const int q = fill[m.h_ids[i]]++;
+    m.h_perm[q] = i;
+    m.h_inv[i] = q;
+  }
+  KIE_HIP(hipMemcpyAsync(m.perm, m.h_perm.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
+  KIE_HIP(hipMemcpyAsync(m.inv, m.h_inv.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
+  if ((rc = ok(kie::launch_gather_rows(hi, lo, d, m.perm, k, m.ch, m.cl, rows, s)))) return rc;
+  const size_t gate_e = (size_t)Fe * d, down_e = (size_t)d * Fe;
+  for (int e = 0; e < E; ++e) {
+    const int cnt = m.off[e + 1] - m.off[e], o = m.off[e];
+    if (cnt == 0) continue;
+    if ((rc = ok(kie::launch_gemm(m.ch + (size_t)o * d, m.cl + (size_t)o * d, d, w.e_gate + e * gate_e, d,
+                                  m.Gc + (size_t)o * Fe, Fe, cnt, Fe, d, false, s))) ||
+        (rc = ok(kie::launch_gemm(m.ch + (size_t)o * d, m.cl + (size_t)o * d, d, w.e_up + e * gate_e, d,
+                                  m.Uc + (size_t)o * Fe, Fe, cnt, Fe, d, false, s))))
+      return rc;
+  }
+  if ((rc = ok(kie::launch_swiglu_w_split(m.Gc, m.Uc, Fe, rows, m.perm, m.wts, m.sh, m.sl, s)))) return rc;
+  for (int e = 0; e < E; ++e) {
+    const int cnt = m.off[e + 1] - m.off[e], o = m.off[e];
+    if (cnt == 0) continue;
+    if ((rc = ok(kie::launch_gemm(m.sh + (size_t)o * Fe, m.sl + (size_t)o * Fe, Fe, w.e_down + e * down_e, Fe,
+                                  m.Yc + (size_t)o * d, d, cnt, d, Fe, false, s))))
+      return rc;
+  }
+  for (int a = 0; a < p.nshared; ++a) {
+    const size_t es = (size_t)(E + a);
+    if ((rc = ok(kie::launch_gemm(hi, lo, d, w.e_gate + es * gate_e, d, m.Gc, Fe, Tn, Fe, d, false, s))) ||
+        (rc = ok(kie::launch_gemm(hi, lo, d, w.e_up + es * gate_e, d, m.Uc, Fe, Tn, Fe, d, false, s))) ||
+        (rc = ok(kie::launch_swiglu_w_split(m.Gc, m.Uc, Fe, Tn, nullptr, nullptr, m.sh, m.sl, s))) ||
+        (rc = ok(kie::launch_gemm(m.sh, m.sl, Fe, w.e_down + es * down_e, Fe, X, d, Tn, d, Fe, true, s))))
+      return rc;
+  }
+  return ok(kie::launch_combine(X, d, m.Yc, m.inv, k, Tn, s));
+}
+
 int prefill_batched(kie_handle* h, int n) {
   const kie::Params& p = h->base;
   const int T = kPrefillChunk;
-  const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = p.F, qkv = qd + 2 * kd;
+  const bool moe = p.E != 0;
+  const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
   const int wide = std::max(std::max(d, qd), F);
   const size_t fbytes = sizeof(float) * (size_t)T * ((size_t)d + qkv + qd + 2 * (size_t)F);
   const size_t hbytes = sizeof(__half) * (size_t)T * wide * 2;
+  // MoE: router logits, routing, compact rows (T * top_k of them)
+  const size_t rk = (size_t)T * (moe ? p.topk : 0), rx = std::max(rk, (size_t)T);
+  const size_t mbytes = moe ? sizeof(float) * ((size_t)T * p.E + rk + 2 * rx * p.Fe + rk * d) +
+                                  sizeof(int) * 3 * rk + sizeof(__half) * (2 * rk * d + 2 * rx * p.Fe)
+                            : 0;
   void* ws = nullptr;
-  hipError_t e = hipMalloc(&ws, fbytes + hbytes);
+  hipError_t e = hipMalloc(&ws, fbytes + hbytes + mbytes);
   if (e != hipSuccess)
     return fail(KIE_ERR_HIP, std::string("prefill workspace hipMalloc failed: ") + hipGetErrorString(e));
+  MoeWs mw{};
+  if (moe) {
+    char* b = static_cast<char*>(ws) + fbytes + hbytes;   // carved in the order of mbytes' terms
+    mw.R = reinterpret_cast<float*>(b); b += sizeof(float) * (size_t)T * p.E;
+    mw.wts = reinterpret_cast<float*>(b); b += sizeof(float) * rk;
+    mw.Gc = reinterpret_cast<float*>(b); b += sizeof(float) * rx * p.Fe;
+    mw.Uc = reinterpret_cast<float*>(b); b += sizeof(float) * rx * p.Fe;
+    mw.Yc = reinterpret_cast<float*>(b); b += sizeof(float) * rk * d;
+    mw.ids = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
+    mw.perm = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
+    mw.inv = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
+    mw.ch = reinterpret_cast<__half*>(b); b += sizeof(__half) * rk * d;
+    mw.cl = reinterpret_cast<__half*>(b); b += sizeof(__half) * rk * d;
+    mw.sh = reinterpret_cast<__half*>(b); b += sizeof(__half) * rx * p.Fe;
+    mw.sl = reinterpret_cast<__half*>(b);
+    mw.h_ids.resize(rk);
+    mw.h_perm.resize(rk);
+    mw.h_inv.resize(rk);
+    mw.off.resize(p.E + 1);
+  }
   float* X = static_cast<float*>(ws);
   float* QKV = X + (size_t)T * d;
   float* O = QKV + (size_t)T * qkv;
@@ -503,11 +595,16 @@ int prefill_batched(kie_handle* h, int n) {
           ok(kie::launch_attn_prefill(QKV, qkv, kc, vc, p.cap, p.H, p.nkv, p.hd, c0, O, Tn, s)) &&
           ok(kie::launch_split(O, qd, hi, lo, Tn, qd, s)) &&
           ok(kie::launch_gemm(hi, lo, qd, w.wo, qd, X, d, Tn, d, qd, true, s)) &&
-          ok(kie::launch_rmsnorm_split(X, w.ffn_norm, d, p.eps, hi, lo, Tn, s)) &&
-          ok(kie::launch_gemm(hi, lo, d, w.w_gate, d, G, F, Tn, F, d, false, s)) &&
-          ok(kie::launch_gemm(hi, lo, d, w.w_up, d, U, F, Tn, F, d, false, s)) &&
-          ok(kie::launch_swiglu_split(G, U, (size_t)Tn * F, hi, lo, s)) &&
-          ok(kie::launch_gemm(hi, lo, F, w.w_down, F, X, d, Tn, d, F, true, s));
+          ok(kie::launch_rmsnorm_split(X, w.ffn_norm, d, p.eps, hi, lo, Tn, s));
+      if (rc != KIE_OK) break;
+      if (moe) {
+        rc = moe_ffn_batched(h, w, l, c0, Tn, hi, lo, X, mw);
+      } else {
+        ok(kie::launch_gemm(hi, lo, d, w.w_gate, d, G, F, Tn, F, d, false, s)) &&
+            ok(kie::launch_gemm(hi, lo, d, w.w_up, d, U, F, Tn, F, d, false, s)) &&
+            ok(kie::launch_swiglu_split(G, U, (size_t)Tn * F, hi, lo, s)) &&
+            ok(kie::launch_gemm(hi, lo, F, w.w_down, F, X, d, Tn, d, F, true, s));
+      }
     }
   }
   e = hipStreamSynchronize(s);
@@ -526,8 +623,7 @@ int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
   if (n < 1) return fail(KIE_ERR_INVALID_ARG, "n_tokens must be >= 1");
   if (n > h->cfg.max_seq) return fail(KIE_ERR_CONTEXT_OVERFLOW, "prompt longer than max_seq");
   const kie::Params& p = h->base;
-  if (p.E != 0) return fail(KIE_ERR_UNSUPPORTED, "batched prefill covers dense models; use kie_prefill");
-  if (p.d % 32 != 0 || (p.H * p.hd) % 32 != 0 || p.F % 32 != 0 || p.hd % 16 != 0)
+  if (p.d % 32 != 0 || (p.H * p.hd) % 32 != 0 || (p.E ? p.Fe : p.F) % 32 != 0 || p.hd % 16 != 0)
     return fail(KIE_ERR_UNSUPPORTED, "batched prefill needs d_model, n_heads*head_dim and ffn_hidden "
                                      "to be multiples of 32 and head_dim of 16; use kie_prefill");
   for (int i = 0; i < n; ++i)

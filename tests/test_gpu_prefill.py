@@ -11,7 +11,7 @@ import pytest
 
 from kie_synth import get_config, make_prompt, make_weights, weights_to_numpy
 from tests.parity import compare_steps
-from tests.test_gpu_parity import _check_kv, _oracle_replay, _say
+from tests.test_gpu_parity import _check_kv, _moe_check, _oracle_replay, _say
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,16 @@ PREFILL_CASES = {
     "longctx_2l_1200": ("longctx", dict(n_layers=2, prompt_len=1200), 8),
     # 3 heads x 128, FFN 864, 4096-row lm_head
     "tp8share_3l": ("tp8share", dict(n_layers=3, prompt_len=96), 16),
+    # 64 routed experts (top 6) + 2 shared, hidden 1408: grouped per-expert products
+    "moe_2l": ("moe", dict(n_layers=2, prompt_len=48), 24),
+    # a narrow MoE over a prompt of two chunks, plain and renormalised weights
+    "moe_narrow_2chunks": ("moe", dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64,
+                                       vocab_in=4096, vocab_out=4096, n_experts=8, top_k=2,
+                                       n_shared_experts=1, expert_hidden=128, prompt_len=700), 16),
+    "moe_narrow_renorm": ("moe", dict(n_layers=2, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64,
+                                      vocab_in=4096, vocab_out=4096, n_experts=8, top_k=2,
+                                      n_shared_experts=1, expert_hidden=128, prompt_len=64,
+                                      moe_renorm=True), 16),
 }
 
 
@@ -82,10 +92,14 @@ def test_prefill_batched_matches_oracle(torch, kie, key):
     toks = toks.cpu().numpy()
     z = z.cpu().numpy()
     o, zo = _oracle_replay(cfg, weights_to_numpy(W), prompt, toks)
-    rep = compare_steps(z, toks, zo)
-    _say(key, rep)
-    assert rep["pinned"] >= n // 2
-    _check_kv(eng, o, range(cfg.n_layers), [(0, min(P - 1, 520)), (max(0, P - 40), P - 1 + n)])
+    # MoE: the routing of every prompt and decode position against the
+    # oracle's (an accepted near-tie excuses that position above layer 0)
+    tied = _moe_check(eng, o, cfg, range(P - 1 + n)) if cfg.is_moe else []
+    rep = compare_steps(z, toks, zo, skip=[q - (P - 1) for q in tied if q >= P - 1])
+    _say(key, rep, "routing near-ties at positions", tied)
+    assert rep["pinned"] >= max(4, n // 4)
+    _check_kv(eng, o, range(cfg.n_layers), [(0, min(P - 1, 520)), (max(0, P - 40), P - 1 + n)],
+              exclude=tied)
     eng.close()
 
 
@@ -135,10 +149,8 @@ def test_prefill_batched_then_staged_graph_decode(torch, kie):
     b.close()
 
 
-def test_prefill_batched_rejects_moe_and_bad_state(torch, kie):
-    cfg = get_config("moe", n_layers=1, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, vocab_in=512,
-                     vocab_out=512, n_experts=4, top_k=2, n_shared_experts=1, expert_hidden=64,
-                     prompt_len=8, n_decode=2)
+def test_prefill_batched_rejects_unsupported_shape_and_bad_state(torch, kie):
+    cfg = get_config("tiny", n_heads=4, head_dim=8, n_kv_heads=4, d_model=256)   # head_dim % 16 != 0
     W = make_weights(cfg, seed=0, device="cuda")
     e = kie.Engine(cfg, W)
     with pytest.raises(kie.KieError) as ei:
