@@ -165,9 +165,9 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * expert_hidden) to be multiples of 32 and head_dim a multiple of 16;
  * otherwise KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace
  * (about 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes, more
- * for MoE) for the call and frees it before returning.  The batched product of a prompt's
- * positions is the step before the decode path (the pages' method is
- * decode; this follows from "matrix cores only in prefill, if at all"). */
+ * for MoE) for the call and frees it before returning.  A prompt's
+ * positions are all known up front, so its products are dense matrix
+ * products; decode steps stay on the GEMV path of the persistent kernel. */
 int kie_prefill_batched(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
 /* Generates n_steps tokens in one launch.  out_tokens: device int32
