@@ -224,7 +224,9 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
 // times the G query heads that share KV head g (blockIdx.y); row r is
 // position r / G, query head g * G + r % G.  It walks the cached positions
 // 0 .. (its last position) in tiles of 32:
-//   S = Q K^T       one 32x32 MFMA tile (wave 0), Q split into fp16 hi + lo;
+//   S = Q K^T       one 32x32 MFMA tile, its hd / 8 steps shared by the 4
+//                   waves and the 4 partial tiles summed in a fixed order;
+//                   Q split into fp16 hi + lo;
 //   online softmax  8 lanes per row: causal mask, running maximum and sum;
 //   O = O f + P V   wave w owns output columns [32 w, 32 w + 32), P split
 //                   into fp16 hi + lo, V staged transposed.
@@ -238,7 +240,7 @@ constexpr int kPS = kMK + 4;
 size_t attn_prefill_lds(int hd) {
   const size_t hdp = (size_t)((hd + 31) & ~31);
   const size_t halves = 3 * (size_t)kMK * attn_qs(hd) + hdp * kPS + 2 * (size_t)kMK * kPS;
-  return sizeof(_Float16) * halves + sizeof(float) * ((size_t)kMK * (kMK + 1) + 3 * kMK);
+  return sizeof(_Float16) * halves + sizeof(float) * (4 * (size_t)kMK * (kMK + 1) + 3 * kMK);
 }
 
 template <int TPR>
@@ -266,8 +268,8 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
   _Float16* Vt = Ks + kMK * qs;                         // [hdp][kPS], V transposed
   _Float16* Ph = Vt + hdp * kPS;                        // [32][kPS]
   _Float16* Pl = Ph + kMK * kPS;
-  float* S = reinterpret_cast<float*>(Pl + kMK * kPS);  // [32][33]
-  float* rm = S + kMK * (kMK + 1);
+  float* S = reinterpret_cast<float*>(Pl + kMK * kPS);  // [4 waves][32][33] partial scores
+  float* rm = S + 4 * kMK * (kMK + 1);
   float* rl = rm + kMK;
   float* rf = rl + kMK;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -316,17 +318,19 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
       for (int i = 0; i < 4; ++i) Vt[(d + i) * kPS + j] = vv[i];
     }
     __syncthreads();
-    if (wave == 0) {
+    {
+      // wave w takes the 8-wide head-dimension steps w, w + 4, ...
       f16acc sa = {};
-      for (int kk = 0; kk < hd; kk += 8) {
+      for (int kk = 8 * wave; kk < hd; kk += 32) {
         const h4 a_h = *reinterpret_cast<const h4*>(&Qh[l32 * qs + kk + kq0]);
         const h4 a_l = *reinterpret_cast<const h4*>(&Ql[l32 * qs + kk + kq0]);
         const h4 b = *reinterpret_cast<const h4*>(&Ks[l32 * qs + kk + kq0]);
         sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, sa, 0, 0, 0);
         sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, sa, 0, 0, 0);
       }
+      float* Sw = S + wave * kMK * (kMK + 1);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) S[(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
+      for (int j = 0; j < 16; ++j) Sw[(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
     }
     __syncthreads();
     {
@@ -335,7 +339,9 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int j = si + 8 * k;
-        float v = S[sr * (kMK + 1) + j];
+        const int si2 = sr * (kMK + 1) + j;
+        constexpr int kW = kMK * (kMK + 1);
+        float v = ((S[si2] + S[kW + si2]) + S[2 * kW + si2]) + S[3 * kW + si2];
         if (!svalid || j >= nk || k0 + j > spos) v = -3.0e38f;
         sc[k] = v;
         mx = fmaxf(mx, v);
