@@ -153,7 +153,7 @@ int kie_create(const kie_config *cfg, const kie_weights *w, void *hip_stream,
 int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
 /* As kie_prefill (same arguments, state afterwards and errors), but the
- * prompt's positions go through each layer together, in chunks of 512:
+ * prompt's positions go through each layer together, in chunks of 2048:
  * the weight products become dense matrix products on the matrix cores
  * (fp16 weights times activations split into fp16 hi + lo parts,
  * accumulated in fp32, so an fp32 product up to rounding order), followed
@@ -164,7 +164,7 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * its rows.  Needs d_model, n_heads * head_dim and ffn_hidden (MoE:
  * expert_hidden) to be multiples of 32 and head_dim a multiple of 16;
  * otherwise KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace
- * (about 512 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes, more
+ * (about 2048 * (2 d + 6 n_heads head_dim + 4 ffn_hidden) * 4 bytes, more
  * for MoE) for the call and frees it before returning.  A prompt's
  * positions are all known up front, so its products are dense matrix
  * products; decode steps stay on the GEMV path of the persistent kernel. */

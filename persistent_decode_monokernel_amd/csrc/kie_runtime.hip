@@ -460,7 +460,7 @@ int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logit
 // Per chunk and layer: RMSNorm -> Q/K/V products -> RoPE + fp16 K/V rows into
 // the cache -> causal attention over the cache -> O product + residual ->
 // RMSNorm -> gate/up products -> SwiGLU -> down product + residual.
-constexpr int kPrefillChunk = 512;
+constexpr int kPrefillChunk = 2048;
 
 // Mixture-of-experts FFN of one chunk and layer (hi/lo hold the normed
 // input): router product, routing per position, positions grouped by expert
