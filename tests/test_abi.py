@@ -107,3 +107,18 @@ def test_sampled_decode_validates_arguments_on_the_host():
     rc = lib.kie_decode_sampled(None, 1, ctypes.c_uint64(1), ctypes.c_float(0.7), None, None)
     assert rc == -1  # KIE_ERR_INVALID_ARG
     assert "handle" in lib.kie_last_error().decode()
+
+
+def test_batched_prefill_and_gemm_validate_arguments_on_the_host():
+    # rejected before anything touches a device: no GPU needed
+    lib = _lib.load()
+    assert lib.kie_prefill_batched(None, None, 1) == -1
+    assert "NULL" in lib.kie_last_error().decode()
+    for m, n, k in ((0, 64, 32), (4, 0, 32), (4, 64, 0), (4, 64, 48), (4, 64, 70000)):
+        assert lib.kie_debug_gemm(None, None, None, m, n, k, 0, None) == -1, (m, n, k)
+        assert "multiple of 32" in lib.kie_last_error().decode()
+
+
+def test_moe_renorm_flag_is_accepted():
+    rc, msg = _with(PRESETS["moe"], flags=0x10)
+    assert rc == 0, msg

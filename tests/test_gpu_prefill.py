@@ -132,6 +132,27 @@ def test_prefill_batched_agrees_with_persistent_prefill(torch, kie):
     b.close()
 
 
+def test_prefill_batched_at_full_capacity(torch, kie):
+    """A prompt that fills the cache but for the pending position: one
+    decode step writes the last row, the next overflows."""
+    cfg = get_config("tiny")
+    W = make_weights(cfg, seed=0, device="cuda")
+    prompt = make_prompt(cfg)
+    P = len(prompt)
+    e = kie.Engine(cfg, W, max_seq=P)
+    e.prefill_batched(prompt)
+    t, z = e.decode(1)
+    torch.cuda.synchronize()
+    assert e.position == P
+    o, zo = _oracle_replay(cfg.with_(max_seq=P), weights_to_numpy(W), prompt, t.cpu().numpy())
+    compare_steps(z.cpu().numpy(), t.cpu().numpy(), zo)
+    _check_kv(e, o, (0, 1), [(P - 8, P)])
+    with pytest.raises(kie.KieError) as ei:
+        e.decode(1)
+    assert ei.value.status == "KIE_ERR_CONTEXT_OVERFLOW"
+    e.close()
+
+
 def test_prefill_batched_then_staged_graph_decode(torch, kie):
     """The staged (hipGraph) mode decodes from the state a batched prefill
     leaves, and matches the persistent kernel decoding from it bit for bit."""
