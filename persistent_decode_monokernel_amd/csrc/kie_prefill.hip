@@ -21,6 +21,7 @@
 namespace kie {
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16acc __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
@@ -42,21 +43,26 @@ __global__ void split_kernel(const float* __restrict__ x, int ldx, __half* __res
 }
 
 // ---------------------------------------------------------------------------
-// C[M][N] (+)= (Ahi + Alo)[M][K] * W[N][K]^T with v_mfma_f32_32x32x8_f16.
+// C[M][N] (+)= (Ahi + Alo)[M][K] * W[N][K]^T with v_mfma_f32_32x32x16_f16,
+// CDNA4's double-rate fp16 MFMA (16 products of the inner index per
+// instruction and output element).
 //
 // Block: 4 waves, a 64 x 64 tile of C; wave (wm, wn) owns a 32 x 32 quarter.
 // K advances kGK = 64 at a time through LDS (rows padded by 8 halves); the
 // next step's tiles are loaded into registers while the current step's
-// MFMAs run.  Operand layout of the 32x32x8 MFMA: lane l holds
-// A[l % 32][4 (l / 32) + i] and B[4 (l / 32) + i][l % 32], i < 4, and
-// accumulator j of lane l is D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32].
-// B[k][n] is W[n][k], so both operands are read as 4 consecutive halves of
-// a row.  Requires K % 32 == 0 and 16-byte aligned rows (lda, ldw multiples
-// of 8); a last step of 32 is zero-padded.
+// MFMAs run.  Operand layout: lane l holds A[l % 32][8 (l / 32) + i] and
+// B[8 (l / 32) + i][l % 32], i < 8, and accumulator j of lane l is
+// D[8 (j / 4) + 4 (l / 32) + j % 4][l % 32].  A and B are read with the same
+// inner-index map, so the contraction is the same whichever of the 16
+// inner positions the unit pairs with each register element.  B[k][n] is
+// W[n][k], so both operands are read as 8 consecutive halves of a row.
+// Requires K % 32 == 0 and 16-byte aligned rows (lda, ldw multiples of 8);
+// a last step of 32 is zero-padded.
 // ---------------------------------------------------------------------------
 constexpr int kGT = 64;
 constexpr int kGK = 64;
 constexpr int kGPad = kGK + 8;
+static_assert(kGPad % 8 == 0, "LDS rows must stay 16-byte aligned for the 8-half operand reads");
 
 // Raw buffer loads: an offset past the resource's size reads zeros, so the
 // ragged rows and the zero-padded last K step need no branches.
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
   const unsigned wbase = (unsigned)((n0 + lr) * ldw + lc) * 2u;
   f16acc acc = {};
   const int ar = (wm + (lane & 31)) * kGPad, br = (wn + (lane & 31)) * kGPad;
-  const int kq0 = 4 * (lane >> 5);
+  const int kin = 8 * (lane >> 5);                 // the lane's inner-index offset
   uint4 h0, h1, l0, l1, w0, w1;
   auto load = [&](int k0) {
     const bool k1in = k0 + 32 < K;
@@ -117,12 +123,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
     __syncthreads();
     if (k0 + kGK < K) load(k0 + kGK);                // in flight during the MFMAs
 #pragma unroll
-    for (int kk = 0; kk < kGK; kk += 8) {
-      const h4 a_h = *reinterpret_cast<const h4*>(&sAh[ar + kk + kq0]);
-      const h4 a_l = *reinterpret_cast<const h4*>(&sAl[ar + kk + kq0]);
-      const h4 b = *reinterpret_cast<const h4*>(&sW[br + kk + kq0]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, acc, 0, 0, 0);
+    for (int kk = 0; kk < kGK; kk += 16) {
+      const h8 a_h = *reinterpret_cast<const h8*>(&sAh[ar + kk + kin]);
+      const h8 a_l = *reinterpret_cast<const h8*>(&sAl[ar + kk + kin]);
+      const h8 b = *reinterpret_cast<const h8*>(&sW[br + kk + kin]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc, 0, 0, 0);
     }
   }
   const int n = n0 + wn + (lane & 31);
@@ -224,18 +230,21 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
 // times the G query heads that share KV head g (blockIdx.y); row r is
 // position r / G, query head g * G + r % G.  It walks the cached positions
 // 0 .. (its last position) in tiles of 32:
-//   S = Q K^T       one 32x32 MFMA tile, its hd / 8 steps shared by the 4
+//   S = Q K^T       one 32x32 MFMA tile, its hd / 16 steps shared by the 4
 //                   waves and the 4 partial tiles summed in a fixed order;
 //                   Q split into fp16 hi + lo;
 //   online softmax  8 lanes per row: causal mask, running maximum and sum;
 //   O = O f + P V   wave w owns output columns [32 w, 32 w + 32), P split
 //                   into fp16 hi + lo, V staged transposed.
+// Both products use v_mfma_f32_32x32x16_f16 with the operand and
+// accumulator layout of the weight product above; LDS rows are padded by 8
+// halves so every 8-half operand read is 16-byte aligned.
 // K and V are the fp16 cache rows (exact in fp16), so every product is an
 // fp32 product up to rounding order.  Needs hd % 16 == 0.
 constexpr int kMK = 32;                       // cached positions per tile (and rows per block)
 
-__host__ __device__ inline int attn_qs(int hd) { return hd + 4; }   // padded row stride (halves)
-constexpr int kPS = kMK + 4;
+__host__ __device__ inline int attn_qs(int hd) { return hd + 8; }   // padded row stride (halves)
+constexpr int kPS = kMK + 8;
 
 size_t attn_prefill_lds(int hd) {
   const size_t hdp = (size_t)((hd + 31) & ~31);
@@ -294,7 +303,8 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
   const __half* K = kc + (size_t)g * cap * hd;
   const __half* V = vc + (size_t)g * cap * hd;
   const int last = pos0 + t0 + tn - 1;
-  const int kq0 = 4 * (lane >> 5), l32 = lane & 31;
+  // kq0: accumulator row offset of the lane; kin: its inner-index offset
+  const int kq0 = 4 * (lane >> 5), kin = 8 * (lane >> 5), l32 = lane & 31;
   // softmax lanes: row sr, lane si of its 8
   const int sr = tid >> 3, si = tid & 7;
   const int stq = sr / G, spos = pos0 + t0 + stq;
@@ -319,14 +329,14 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
     }
     __syncthreads();
     {
-      // wave w takes the 8-wide head-dimension steps w, w + 4, ...
+      // wave w takes the 16-wide head-dimension steps w, w + 4, ...
       f16acc sa = {};
-      for (int kk = 8 * wave; kk < hd; kk += 32) {
-        const h4 a_h = *reinterpret_cast<const h4*>(&Qh[l32 * qs + kk + kq0]);
-        const h4 a_l = *reinterpret_cast<const h4*>(&Ql[l32 * qs + kk + kq0]);
-        const h4 b = *reinterpret_cast<const h4*>(&Ks[l32 * qs + kk + kq0]);
-        sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, sa, 0, 0, 0);
-        sa = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, sa, 0, 0, 0);
+      for (int kk = 16 * wave; kk < hd; kk += 64) {
+        const h8 a_h = *reinterpret_cast<const h8*>(&Qh[l32 * qs + kk + kin]);
+        const h8 a_l = *reinterpret_cast<const h8*>(&Ql[l32 * qs + kk + kin]);
+        const h8 b = *reinterpret_cast<const h8*>(&Ks[l32 * qs + kk + kin]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, sa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, sa, 0, 0, 0);
       }
       float* Sw = S + wave * kMK * (kMK + 1);
 #pragma unroll
@@ -369,12 +379,12 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[j] *= rf[8 * (j >> 2) + kq0 + (j & 3)];
 #pragma unroll
-      for (int kk = 0; kk < kMK; kk += 8) {
-        const h4 a_h = *reinterpret_cast<const h4*>(&Ph[l32 * kPS + kk + kq0]);
-        const h4 a_l = *reinterpret_cast<const h4*>(&Pl[l32 * kPS + kk + kq0]);
-        const h4 b = *reinterpret_cast<const h4*>(&Vt[(wave * 32 + l32) * kPS + kk + kq0]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, acc, 0, 0, 0);
+      for (int kk = 0; kk < kMK; kk += 16) {
+        const h8 a_h = *reinterpret_cast<const h8*>(&Ph[l32 * kPS + kk + kin]);
+        const h8 a_l = *reinterpret_cast<const h8*>(&Pl[l32 * kPS + kk + kin]);
+        const h8 b = *reinterpret_cast<const h8*>(&Vt[(wave * 32 + l32) * kPS + kk + kin]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc, 0, 0, 0);
       }
     }
     __syncthreads();

@@ -530,7 +530,7 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
 
 int prefill_batched(kie_handle* h, int n) {
   const kie::Params& p = h->base;
-  const int T = kPrefillChunk;
+  const int T = std::max(1, std::min(kPrefillChunk, n - 1));   // positions per chunk (workspace rows)
   const bool moe = p.E != 0;
   const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
   const int wide = std::max(std::max(d, qd), F);
