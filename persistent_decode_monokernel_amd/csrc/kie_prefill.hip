@@ -226,177 +226,174 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
 }
 
 // Causal attention over the cache for a chunk's positions, on the matrix
-// cores.  A block takes 32 rows: 32 / G consecutive positions of the chunk
-// times the G query heads that share KV head g (blockIdx.y); row r is
-// position r / G, query head g * G + r % G.  It walks the cached positions
-// 0 .. (its last position) in tiles of 32:
-//   S = Q K^T       one 32x32 MFMA tile, its hd / 16 steps shared by the 4
-//                   waves and the 4 partial tiles summed in a fixed order;
-//                   Q split into fp16 hi + lo;
-//   online softmax  8 lanes per row: causal mask, running maximum and sum;
-//   O = O f + P V   wave w owns output columns [32 w, 32 w + 32), P split
-//                   into fp16 hi + lo, V staged transposed.
+// cores.  A block of 4 waves takes 128 rows: 128 / G consecutive positions
+// of the chunk times the G query heads that share KV head g (blockIdx.y);
+// row r is position r / G, query head g * G + r % G, and wave w owns rows
+// [32 w, 32 w + 32).  The block walks the cached positions 0 .. (its last
+// position) in tiles of 32, staged once in LDS for all four waves:
+//   S = Q K^T       per wave one 32x32 MFMA tile over hd / 16 steps, Q held
+//                   in registers as fp16 hi + lo;
+//   online softmax  2 lanes per row: causal mask, running maximum and sum;
+//   O = O f + P V   per wave hd / 32 (rounded up) column tiles, P split into
+//                   fp16 hi + lo, V staged transposed.
 // Both products use v_mfma_f32_32x32x16_f16 with the operand and
 // accumulator layout of the weight product above; LDS rows are padded by 8
-// halves so every 8-half operand read is 16-byte aligned.
-// K and V are the fp16 cache rows (exact in fp16), so every product is an
-// fp32 product up to rounding order.  Needs hd % 16 == 0.
-constexpr int kMK = 32;                       // cached positions per tile (and rows per block)
+// halves so every 8-half operand read is 16-byte aligned.  K and V are the
+// fp16 cache rows, so every product is fp32 up to rounding order.
+constexpr int kMK = 32;                       // cached positions per tile
+constexpr int kAW = 4;                        // waves per block
+constexpr int kAR = 32 * kAW;                 // query rows per block
+constexpr int kQS = kMaxHeadDim + 8;          // K tile row stride (halves)
+constexpr int kPS = kMK + 8;                  // P and transposed V row stride (halves)
+static_assert(kQS % 8 == 0 && kPS % 8 == 0, "LDS rows must stay 16-byte aligned");
 
-__host__ __device__ inline int attn_qs(int hd) { return hd + 8; }   // padded row stride (halves)
-constexpr int kPS = kMK + 8;
-
-size_t attn_prefill_lds(int hd) {
-  const size_t hdp = (size_t)((hd + 31) & ~31);
-  const size_t halves = 3 * (size_t)kMK * attn_qs(hd) + hdp * kPS + 2 * (size_t)kMK * kPS;
-  return sizeof(_Float16) * halves + sizeof(float) * (4 * (size_t)kMK * (kMK + 1) + 3 * kMK);
-}
-
-template <int TPR>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = 1; o < TPR; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-template <int TPR>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
+template <int NS>   // NS = hd / 16 inner steps of the score product
 __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
                                                           const __half* __restrict__ kc,
                                                           const __half* __restrict__ vc, int cap, int H,
-                                                          int nkv, int hd, int pos0, int T, float* __restrict__ O) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int G = H / nkv, QP = kMK / G, hdp = (hd + 31) & ~31, qs = attn_qs(hd);
-  _Float16* Qh = reinterpret_cast<_Float16*>(lds);     // [32][qs]
-  _Float16* Ql = Qh + kMK * qs;
-  _Float16* Ks = Ql + kMK * qs;                         // [32][qs]
-  _Float16* Vt = Ks + kMK * qs;                         // [hdp][kPS], V transposed
-  _Float16* Ph = Vt + hdp * kPS;                        // [32][kPS]
-  _Float16* Pl = Ph + kMK * kPS;
-  float* S = reinterpret_cast<float*>(Pl + kMK * kPS);  // [4 waves][32][33] partial scores
-  float* rm = S + 4 * kMK * (kMK + 1);
-  float* rl = rm + kMK;
-  float* rf = rl + kMK;
+                                                          int nkv, int pos0, int T, float* __restrict__ O) {
+  constexpr int hd = 16 * NS, NCT = (NS + 1) / 2, hdp = 32 * NCT;
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[kMK * kQS];       // [key][dim]
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[kMaxHeadDim * kPS];   // [dim][key]
+  __shared__ __attribute__((aligned(16))) _Float16 Ph[kAW][32 * kPS];
+  __shared__ __attribute__((aligned(16))) _Float16 Pl[kAW][32 * kPS];
+  __shared__ float Sw[kAW][32 * (kMK + 1)];
+  __shared__ float rfw[kAW][32];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = H / nkv, QP = kAR / G;
   const int t0 = blockIdx.x * QP, g = blockIdx.y;
   const int tn = min(QP, T - t0);
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int e = tid; e < kMK * hd; e += kPT) {
-    const int r = e / hd, d = e - r * hd;
-    const int tq = r / G, h = g * G + r % G;
-    const float v = tq < tn ? QKV[(size_t)(t0 + tq) * ldq + h * hd + d] * scale : 0.f;
-    const _Float16 hi = (_Float16)v;
-    Qh[r * qs + d] = hi;
-    Ql[r * qs + d] = (_Float16)(v - (float)hi);
-  }
-  for (int e = tid; e < (hdp - hd) * kPS; e += kPT) Vt[hd * kPS + e] = (_Float16)0.f;   // padded columns
-  if (tid < kMK) {
-    rm[tid] = -3.0e38f;
-    rl[tid] = 0.f;
-  }
-  f16acc acc = {};
-  const bool pv = wave * 32 < hdp;
-  const __half* K = kc + (size_t)g * cap * hd;
-  const __half* V = vc + (size_t)g * cap * hd;
-  const int last = pos0 + t0 + tn - 1;
   // kq0: accumulator row offset of the lane; kin: its inner-index offset
   const int kq0 = 4 * (lane >> 5), kin = 8 * (lane >> 5), l32 = lane & 31;
-  // softmax lanes: row sr, lane si of its 8
-  const int sr = tid >> 3, si = tid & 7;
-  const int stq = sr / G, spos = pos0 + t0 + stq;
+  // this lane's query row as an MFMA A operand, split hi/lo, per 16-wide step
+  h8 qh[NS], ql[NS];
+  {
+    const int r = wave * 32 + l32, tq = r / G, h = g * G + r % G;
+    const float* q = QKV + (size_t)(t0 + tq) * ldq + h * hd + kin;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = tq < tn ? q[16 * s + i] * scale : 0.f;
+        const _Float16 hi = (_Float16)v;
+        qh[s][i] = hi;
+        ql[s][i] = (_Float16)(v - (float)hi);
+      }
+    }
+  }
+  for (int e = tid; e < (hdp - hd) * kPS; e += kPT) Vt[hd * kPS + e] = (_Float16)0.f;   // padded columns
+  // softmax lanes: row sr of the wave, keys si, si + 2, ... of the tile
+  const int sr = lane >> 1, si = lane & 1;
+  const int stq = (wave * 32 + sr) / G, spos = pos0 + t0 + stq;
   const bool svalid = stq < tn;
-  __syncthreads();
+  float rm = -3.0e38f, rl = 0.f;
+  // the wave's last position, and the block's
+  const int wlast = pos0 + t0 + min(tn - 1, (wave * 32 + 31) / G);
+  const bool wactive = wave * 32 / G < tn;
+  const int last = pos0 + t0 + tn - 1;
+  f16acc acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = (f16acc){};
+  const __half* K = kc + (size_t)g * cap * hd;
+  const __half* V = vc + (size_t)g * cap * hd;
   for (int k0 = 0; k0 <= last; k0 += kMK) {
     const int nk = min(kMK, last + 1 - k0);
-    const int hd4 = hd >> 2;
-    for (int e = tid; e < kMK * hd4; e += kPT) {          // 4 halves (8 bytes) at a time
-      const int j = e / hd4, d = 4 * (e - j * hd4);
-      const bool in = j < nk;
-      const size_t src = (size_t)(k0 + (in ? j : 0)) * hd + d;
-      h4 kv = *reinterpret_cast<const h4*>(K + src);
-      h4 vv = *reinterpret_cast<const h4*>(V + src);
-      if (!in) {
-        kv = (h4){0, 0, 0, 0};
-        vv = (h4){0, 0, 0, 0};
+    const bool run = wactive && k0 <= wlast;        // the tile holds keys some row of the wave sees
+    __syncthreads();                                 // the previous tile's reads are done
+    constexpr int kC = hd / 8;                       // 16-byte chunks per row
+    for (int e = tid; e < kMK * kC; e += kPT) {
+      // K: chunks of one row on neighbouring lanes; V: rows on neighbouring lanes
+      {
+        const int j = e / kC, c = e - j * kC;
+        uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + (j < nk ? j : 0)) * hd + 8 * c);
+        if (j >= nk) kv = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(&Ks[j * kQS + 8 * c]) = kv;
       }
-      *reinterpret_cast<h4*>(&Ks[j * qs + d]) = kv;
+      {
+        const int j = e & (kMK - 1), c = e / kMK;
+        h8 vv = *reinterpret_cast<const h8*>(V + (size_t)(k0 + (j < nk ? j : 0)) * hd + 8 * c);
+        if (j >= nk) vv = (h8){};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Vt[(d + i) * kPS + j] = vv[i];
+        for (int i = 0; i < 8; ++i) Vt[(8 * c + i) * kPS + j] = vv[i];
+      }
     }
     __syncthreads();
-    {
-      // wave w takes the 16-wide head-dimension steps w, w + 4, ...
+    if (run) {
       f16acc sa = {};
-      for (int kk = 16 * wave; kk < hd; kk += 64) {
-        const h8 a_h = *reinterpret_cast<const h8*>(&Qh[l32 * qs + kk + kin]);
-        const h8 a_l = *reinterpret_cast<const h8*>(&Ql[l32 * qs + kk + kin]);
-        const h8 b = *reinterpret_cast<const h8*>(&Ks[l32 * qs + kk + kin]);
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, sa, 0, 0, 0);
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, sa, 0, 0, 0);
-      }
-      float* Sw = S + wave * kMK * (kMK + 1);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) Sw[(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
+      for (int s = 0; s < NS; ++s) {
+        const h8 b = *reinterpret_cast<const h8*>(&Ks[l32 * kQS + 16 * s + kin]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[s], b, sa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql[s], b, sa, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) Sw[wave][(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
     }
     __syncthreads();
-    {
-      float sc[4];
-      float mx = rm[sr];
+    if (run) {
+      float sc[16];
+      float mx = rm;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = si + 8 * k;
-        const int si2 = sr * (kMK + 1) + j;
-        constexpr int kW = kMK * (kMK + 1);
-        float v = ((S[si2] + S[kW + si2]) + S[2 * kW + si2]) + S[3 * kW + si2];
+      for (int k = 0; k < 16; ++k) {
+        const int j = si + 2 * k;
+        float v = Sw[wave][sr * (kMK + 1) + j];
         if (!svalid || j >= nk || k0 + j > spos) v = -3.0e38f;
         sc[k] = v;
         mx = fmaxf(mx, v);
       }
-      mx = group_max<8>(mx);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
       float sum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 16; ++k) {
         const float pk = sc[k] > -1.0e38f ? __expf(sc[k] - mx) : 0.f;
         const _Float16 hi = (_Float16)pk;
-        Ph[sr * kPS + si + 8 * k] = hi;
-        Pl[sr * kPS + si + 8 * k] = (_Float16)(pk - (float)hi);
+        Ph[wave][sr * kPS + si + 2 * k] = hi;
+        Pl[wave][sr * kPS + si + 2 * k] = (_Float16)(pk - (float)hi);
         sum += pk;
       }
-      sum = group_sum<8>(sum);
-      if (si == 0) {
-        const float f = __expf(rm[sr] - mx);
-        rf[sr] = f;
-        rl[sr] = rl[sr] * f + sum;
-        rm[sr] = mx;
-      }
+      sum += __shfl_xor(sum, 1, 64);
+      const float f = __expf(rm - mx);
+      rl = rl * f + sum;
+      rm = mx;
+      if (si == 0) rfw[wave][sr] = f;
     }
     __syncthreads();
-    if (pv) {
+    if (run) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] *= rf[8 * (j >> 2) + kq0 + (j & 3)];
+      for (int c = 0; c < NCT; ++c) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[c][j] *= rfw[wave][8 * (j >> 2) + kq0 + (j & 3)];
+      }
 #pragma unroll
       for (int kk = 0; kk < kMK; kk += 16) {
-        const h8 a_h = *reinterpret_cast<const h8*>(&Ph[l32 * kPS + kk + kin]);
-        const h8 a_l = *reinterpret_cast<const h8*>(&Pl[l32 * kPS + kk + kin]);
-        const h8 b = *reinterpret_cast<const h8*>(&Vt[(wave * 32 + l32) * kPS + kk + kin]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc, 0, 0, 0);
+        const h8 a_h = *reinterpret_cast<const h8*>(&Ph[wave][l32 * kPS + kk + kin]);
+        const h8 a_l = *reinterpret_cast<const h8*>(&Pl[wave][l32 * kPS + kk + kin]);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          const h8 b = *reinterpret_cast<const h8*>(&Vt[(32 * c + l32) * kPS + kk + kin]);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc[c], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
   }
-  if (pv) {
-    const int d = wave * 32 + l32;
+  // the row sums, from the softmax lanes to the accumulator lanes
+  __syncthreads();
+  if (si == 0) rfw[wave][sr] = rl;
+  __syncthreads();
+  if (!wactive) return;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = 8 * (j >> 2) + kq0 + (j & 3);
-      const int tq = r / G;
-      if (tq < tn && d < hd)
-        O[(size_t)(t0 + tq) * H * hd + (g * G + r % G) * hd + d] = acc[j] / rl[r];
+  for (int j = 0; j < 16; ++j) {
+    const int rw = 8 * (j >> 2) + kq0 + (j & 3), r = wave * 32 + rw;
+    const int tq = r / G;
+    if (tq >= tn) continue;
+    const float l = rfw[wave][rw];
+    float* out = O + (size_t)(t0 + tq) * H * hd + (g * G + r % G) * hd;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int d = 32 * c + l32;
+      if (d < hd) out[d] = acc[c][j] / l;
     }
   }
 }
@@ -531,10 +528,19 @@ hipError_t launch_rope_kv(float* QKV, int ldq, int H, int nkv, int hd, int pos0,
 }
 hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, const __half* vc, int cap, int H,
                                int nkv, int hd, int pos0, float* O, int T, hipStream_t s) {
-  const size_t lds = attn_prefill_lds(hd);          // < 64 KiB for every head size <= 128
-  const int qp = kMK / (H / nkv);
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3((T + qp - 1) / qp, nkv), dim3(kPT), lds, s, QKV, ldq, kc, vc,
-                     cap, H, nkv, hd, pos0, T, O);
+  const int qp = kAR / (H / nkv);                   // positions per block (H / nkv is 1, 2 or 4)
+  const dim3 grid((T + qp - 1) / qp, nkv);
+  switch (hd / 16) {
+#define KIE_ATTN_CASE(ns)                                                                                     \
+  case ns:                                                                                                    \
+    hipLaunchKernelGGL(attn_prefill_kernel<ns>, grid, dim3(kPT), 0, s, QKV, ldq, kc, vc, cap, H, nkv, pos0, T, O); \
+    break;
+    KIE_ATTN_CASE(1) KIE_ATTN_CASE(2) KIE_ATTN_CASE(3) KIE_ATTN_CASE(4)
+    KIE_ATTN_CASE(5) KIE_ATTN_CASE(6) KIE_ATTN_CASE(7) KIE_ATTN_CASE(8)
+#undef KIE_ATTN_CASE
+    default:
+      return hipErrorInvalidValue;                  // head_dim must be 16, 32, ..., 128
+  }
   return hipGetLastError();
 }
 hipError_t launch_swiglu_split(const float* G, const float* U, size_t n, __half* hi, __half* lo,
