@@ -101,6 +101,10 @@ hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, uns
 hipError_t launch_split(const float* x, int ldx, __half* hi, __half* lo, int M, int K, hipStream_t s);
 hipError_t launch_gemm(const __half* ahi, const __half* alo, int lda, const __half* w, int ldw, float* c,
                        int ldc, int M, int N, int K, bool accumulate, hipStream_t s);
+// tiles: device int[3 * ntiles] of (first row, end row, weight index), at most 64 rows each
+hipError_t launch_gemm_grouped(const __half* ahi, const __half* alo, int lda, const __half* w, size_t wstride,
+                               int ldw, float* c, int ldc, const int* tiles, int ntiles, int N, int K,
+                               hipStream_t s);
 hipError_t launch_embed(const __half* emb, const int* tok, int d, float* X, int T, hipStream_t s);
 hipError_t launch_rmsnorm_split(const float* X, const __half* gain, int d, float eps, __half* hi, __half* lo,
                                 int T, hipStream_t s);

@@ -74,16 +74,28 @@ __device__ __forceinline__ uint4 gemm_ld(__amdgpu_buffer_rsrc_t r, unsigned off)
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+//
+// Grouped form (tiles != nullptr): row block y takes the rows [tiles[3y],
+// tiles[3y + 1]) of A and C (at most 64) and the weight matrix
+// w + tiles[3y + 2] * wstride, so the products of several experts over
+// their own rows of one compact A run as one launch.
 __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ahi,
                                                    const __half* __restrict__ alo, int lda,
                                                    const __half* __restrict__ w, int ldw,
                                                    float* __restrict__ c, int ldc, int M, int N, int K,
-                                                   int accumulate) {
+                                                   int accumulate, const int* __restrict__ tiles,
+                                                   size_t wstride) {
   __shared__ __attribute__((aligned(16))) _Float16 sAh[kGT * kGPad];
   __shared__ __attribute__((aligned(16))) _Float16 sAl[kGT * kGPad];
   __shared__ __attribute__((aligned(16))) _Float16 sW[kGT * kGPad];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
+  int m0 = blockIdx.y * kGT;
+  const int n0 = blockIdx.x * kGT;
+  if (tiles) {
+    m0 = tiles[3 * blockIdx.y];
+    M = tiles[3 * blockIdx.y + 1];
+    w += (size_t)tiles[3 * blockIdx.y + 2] * wstride;
+  }
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   // loader: row lr, 8 halves at columns lc and lc + 32 of each 64-wide step
   const int lr = tid >> 2, lc = (tid & 3) * 8;
@@ -563,7 +575,16 @@ hipError_t launch_gemm(const __half* ahi, const __half* alo, int lda, const __ha
                        int ldc, int M, int N, int K, bool accumulate, hipStream_t s) {
   const dim3 grid((N + kGT - 1) / kGT, (M + kGT - 1) / kGT);
   hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, M, N, K,
-                     accumulate ? 1 : 0);
+                     accumulate ? 1 : 0, (const int*)nullptr, (size_t)0);
+  return hipGetLastError();
+}
+hipError_t launch_gemm_grouped(const __half* ahi, const __half* alo, int lda, const __half* w, size_t wstride,
+                               int ldw, float* c, int ldc, const int* tiles, int ntiles, int N, int K,
+                               hipStream_t s) {
+  if (ntiles == 0) return hipSuccess;
+  const dim3 grid((N + kGT - 1) / kGT, ntiles);
+  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, 0, N, K, 0, tiles,
+                     wstride);
   return hipGetLastError();
 }
 

@@ -464,14 +464,18 @@ constexpr int kPrefillChunk = 2048;
 
 // Mixture-of-experts FFN of one chunk and layer (hi/lo hold the normed
 // input): router product, routing per position, positions grouped by expert
-// on the host, per-expert products over the grouped rows, shared experts over
-// all rows, and the weighted expert outputs summed back in rank order.
+// on the host, the routed experts' products over their grouped rows as one
+// grouped launch per product, shared experts over all rows, and the weighted
+// expert outputs summed back in rank order.
 struct MoeWs {
   float *R, *wts, *Gc, *Uc, *Yc;
-  int *ids, *perm, *inv;
+  int *ids, *perm, *inv, *tiles;
   __half *ch, *cl, *sh, *sl;
-  std::vector<int> h_ids, h_perm, h_inv, off;
+  std::vector<int> h_ids, h_perm, h_inv, h_tiles, off;
 };
+
+// Row tiles of the grouped products: at most rows / 64 + E of them.
+size_t moe_max_tiles(size_t rows, int E) { return rows / 64 + (size_t)E + 1; }
 
 int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int Tn, const __half* hi,
                     const __half* lo, float* X, MoeWs& m) {
@@ -496,27 +500,24 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
     m.h_perm[q] = i;
     m.h_inv[i] = q;
   }
+  // row tiles of at most 64 rows that never straddle two experts
+  int nt = 0;
+  for (int e = 0; e < E; ++e)
+    for (int r0 = m.off[e]; r0 < m.off[e + 1]; r0 += 64, ++nt) {
+      m.h_tiles[3 * nt] = r0;
+      m.h_tiles[3 * nt + 1] = std::min(r0 + 64, m.off[e + 1]);
+      m.h_tiles[3 * nt + 2] = e;
+    }
   KIE_HIP(hipMemcpyAsync(m.perm, m.h_perm.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
   KIE_HIP(hipMemcpyAsync(m.inv, m.h_inv.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
+  KIE_HIP(hipMemcpyAsync(m.tiles, m.h_tiles.data(), sizeof(int) * 3 * nt, hipMemcpyHostToDevice, s));
   if ((rc = ok(kie::launch_gather_rows(hi, lo, d, m.perm, k, m.ch, m.cl, rows, s)))) return rc;
   const size_t gate_e = (size_t)Fe * d, down_e = (size_t)d * Fe;
-  for (int e = 0; e < E; ++e) {
-    const int cnt = m.off[e + 1] - m.off[e], o = m.off[e];
-    if (cnt == 0) continue;
-    if ((rc = ok(kie::launch_gemm(m.ch + (size_t)o * d, m.cl + (size_t)o * d, d, w.e_gate + e * gate_e, d,
-                                  m.Gc + (size_t)o * Fe, Fe, cnt, Fe, d, false, s))) ||
-        (rc = ok(kie::launch_gemm(m.ch + (size_t)o * d, m.cl + (size_t)o * d, d, w.e_up + e * gate_e, d,
-                                  m.Uc + (size_t)o * Fe, Fe, cnt, Fe, d, false, s))))
-      return rc;
-  }
-  if ((rc = ok(kie::launch_swiglu_w_split(m.Gc, m.Uc, Fe, rows, m.perm, m.wts, m.sh, m.sl, s)))) return rc;
-  for (int e = 0; e < E; ++e) {
-    const int cnt = m.off[e + 1] - m.off[e], o = m.off[e];
-    if (cnt == 0) continue;
-    if ((rc = ok(kie::launch_gemm(m.sh + (size_t)o * Fe, m.sl + (size_t)o * Fe, Fe, w.e_down + e * down_e, Fe,
-                                  m.Yc + (size_t)o * d, d, cnt, d, Fe, false, s))))
-      return rc;
-  }
+  if ((rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_gate, gate_e, d, m.Gc, Fe, m.tiles, nt, Fe, d, s))) ||
+      (rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_up, gate_e, d, m.Uc, Fe, m.tiles, nt, Fe, d, s))) ||
+      (rc = ok(kie::launch_swiglu_w_split(m.Gc, m.Uc, Fe, rows, m.perm, m.wts, m.sh, m.sl, s))) ||
+      (rc = ok(kie::launch_gemm_grouped(m.sh, m.sl, Fe, w.e_down, down_e, Fe, m.Yc, d, m.tiles, nt, d, Fe, s))))
+    return rc;
   for (int a = 0; a < p.nshared; ++a) {
     const size_t es = (size_t)(E + a);
     if ((rc = ok(kie::launch_gemm(hi, lo, d, w.e_gate + es * gate_e, d, m.Gc, Fe, Tn, Fe, d, false, s))) ||
@@ -536,33 +537,49 @@ int prefill_batched(kie_handle* h, int n) {
   const int wide = std::max(std::max(d, qd), F);
   const size_t fbytes = sizeof(float) * (size_t)T * ((size_t)d + qkv + qd + 2 * (size_t)F);
   const size_t hbytes = sizeof(__half) * (size_t)T * wide * 2;
-  // MoE: router logits, routing, compact rows (T * top_k of them)
+  // MoE: router logits, routing, compact rows (T * top_k of them), the row
+  // tiles of the grouped products; each region starts 256-byte aligned
   const size_t rk = (size_t)T * (moe ? p.topk : 0), rx = std::max(rk, (size_t)T);
-  const size_t mbytes = moe ? sizeof(float) * ((size_t)T * p.E + rk + 2 * rx * p.Fe + rk * d) +
-                                  sizeof(int) * 3 * rk + sizeof(__half) * (2 * rk * d + 2 * rx * p.Fe)
-                            : 0;
+  const size_t mbase = (fbytes + hbytes + 255) & ~(size_t)255;
+  size_t mo[13] = {}, mbytes = 0;
+  if (moe) {
+    const size_t Fe = p.Fe, rows_d = rk * d, ntile = moe_max_tiles(rk, p.E);
+    const size_t sz[13] = {sizeof(float) * (size_t)T * p.E, sizeof(float) * rk,   // R, wts
+                           sizeof(float) * rx * Fe, sizeof(float) * rx * Fe,      // Gc, Uc
+                           sizeof(float) * rows_d,                                // Yc
+                           sizeof(int) * rk, sizeof(int) * rk, sizeof(int) * rk,  // ids, perm, inv
+                           sizeof(int) * 3 * ntile,                               // tiles
+                           sizeof(__half) * rows_d, sizeof(__half) * rows_d,      // ch, cl
+                           sizeof(__half) * rx * Fe, sizeof(__half) * rx * Fe};   // sh, sl
+    for (int i = 0; i < 13; ++i) {
+      mo[i] = mbytes;
+      mbytes += (sz[i] + 255) & ~(size_t)255;
+    }
+  }
   void* ws = nullptr;
-  hipError_t e = hipMalloc(&ws, fbytes + hbytes + mbytes);
+  hipError_t e = hipMalloc(&ws, mbase + mbytes);
   if (e != hipSuccess)
     return fail(KIE_ERR_HIP, std::string("prefill workspace hipMalloc failed: ") + hipGetErrorString(e));
   MoeWs mw{};
   if (moe) {
-    char* b = static_cast<char*>(ws) + fbytes + hbytes;   // carved in the order of mbytes' terms
-    mw.R = reinterpret_cast<float*>(b); b += sizeof(float) * (size_t)T * p.E;
-    mw.wts = reinterpret_cast<float*>(b); b += sizeof(float) * rk;
-    mw.Gc = reinterpret_cast<float*>(b); b += sizeof(float) * rx * p.Fe;
-    mw.Uc = reinterpret_cast<float*>(b); b += sizeof(float) * rx * p.Fe;
-    mw.Yc = reinterpret_cast<float*>(b); b += sizeof(float) * rk * d;
-    mw.ids = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
-    mw.perm = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
-    mw.inv = reinterpret_cast<int*>(b); b += sizeof(int) * rk;
-    mw.ch = reinterpret_cast<__half*>(b); b += sizeof(__half) * rk * d;
-    mw.cl = reinterpret_cast<__half*>(b); b += sizeof(__half) * rk * d;
-    mw.sh = reinterpret_cast<__half*>(b); b += sizeof(__half) * rx * p.Fe;
-    mw.sl = reinterpret_cast<__half*>(b);
+    char* b = static_cast<char*>(ws) + mbase;
+    mw.R = reinterpret_cast<float*>(b + mo[0]);
+    mw.wts = reinterpret_cast<float*>(b + mo[1]);
+    mw.Gc = reinterpret_cast<float*>(b + mo[2]);
+    mw.Uc = reinterpret_cast<float*>(b + mo[3]);
+    mw.Yc = reinterpret_cast<float*>(b + mo[4]);
+    mw.ids = reinterpret_cast<int*>(b + mo[5]);
+    mw.perm = reinterpret_cast<int*>(b + mo[6]);
+    mw.inv = reinterpret_cast<int*>(b + mo[7]);
+    mw.tiles = reinterpret_cast<int*>(b + mo[8]);
+    mw.ch = reinterpret_cast<__half*>(b + mo[9]);
+    mw.cl = reinterpret_cast<__half*>(b + mo[10]);
+    mw.sh = reinterpret_cast<__half*>(b + mo[11]);
+    mw.sl = reinterpret_cast<__half*>(b + mo[12]);
     mw.h_ids.resize(rk);
     mw.h_perm.resize(rk);
     mw.h_inv.resize(rk);
+    mw.h_tiles.resize(3 * moe_max_tiles(rk, p.E));
     mw.off.resize(p.E + 1);
   }
   float* X = static_cast<float*>(ws);
