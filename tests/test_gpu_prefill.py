@@ -32,10 +32,12 @@ def kie():
 
 @pytest.mark.parametrize("m,n,k,acc", [(1, 64, 32, False), (5, 100, 64, True), (64, 64, 2560, False),
                                        (130, 200, 2560, True), (77, 2560, 6912, False),
-                                       (513, 384, 864, True)])
+                                       (513, 384, 864, True), (2048, 2560, 2560, False),
+                                       (2100, 2100, 96, True)])
 def test_gemm_matches_float64(torch, kie, m, n, k, acc):
     """Tiles that cover the 64 x 64 block, ragged edges in m and n, the
-    accumulate form, and the inner sizes of the workloads."""
+    accumulate form, and the inner sizes of the workloads, up to a full
+    2048-position chunk of the long-context shape."""
     _say("gemm", m, n, k, acc)
     g = torch.Generator(device="cuda").manual_seed(m * 7 + n * 3 + k)
     w = (torch.randn(n, k, device="cuda", generator=g) * 0.02).half()
@@ -61,6 +63,8 @@ PREFILL_CASES = {
     "gqa2_narrow": ("tiny", dict(n_heads=8, n_kv_heads=4, head_dim=32, prompt_len=80), 16),
     # grouped-query attention 32 x 80 over 8 KV heads, a 1200-position prompt
     "longctx_2l_1200": ("longctx", dict(n_layers=2, prompt_len=1200), 8),
+    # a full first chunk of 2048 positions, then a ragged second one
+    "longctx_2l_2150": ("longctx", dict(n_layers=2, prompt_len=2150), 8),
     # a narrow dense model over two chunks of 2048 positions
     "tiny_2chunks": ("tiny", dict(prompt_len=2300), 16),
     # 3 heads x 128, FFN 864, 4096-row lm_head
