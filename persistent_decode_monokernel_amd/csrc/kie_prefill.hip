@@ -248,12 +248,22 @@ __global__ __launch_bounds__(kPT) void rope_kv_kernel(float* __restrict__ QKV, i
 //   online softmax  2 lanes per row: causal mask, running maximum and sum;
 //   O = O f + P V   per wave hd / 32 (rounded up) column tiles, P split into
 //                   fp16 hi + lo, V staged transposed.
+// Scores, P and the rescale factors are per wave, so only the K/V staging
+// takes block barriers (two per tile); the rest is ordered within the wave.
 // Both products use v_mfma_f32_32x32x16_f16 with the operand and
 // accumulator layout of the weight product above; LDS rows are padded by 8
 // halves so every 8-half operand read is 16-byte aligned.  K and V are the
 // fp16 cache rows, so every product is fp32 up to rounding order.
 constexpr int kMK = 32;                       // cached positions per tile
 constexpr int kAW = 4;                        // waves per block
+
+// The LDS writes of the calling wave are complete and visible to all its
+// lanes (a wave-scope release/acquire around the wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 constexpr int kAR = 32 * kAW;                 // query rows per block
 constexpr int kQS = kMaxHeadDim + 8;          // K tile row stride (halves)
 constexpr int kPS = kMK + 8;                  // P and transposed V row stride (halves)
@@ -309,28 +319,44 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
   for (int c = 0; c < NCT; ++c) acc[c] = (f16acc){};
   const __half* K = kc + (size_t)g * cap * hd;
   const __half* V = vc + (size_t)g * cap * hd;
+  // K/V tile staging: 16-byte chunks e = tid, tid + 256 of the tile's 32 rows;
+  // K puts a row's chunks on neighbouring lanes, V the rows.  The next tile
+  // is loaded into registers while the current one is computed.
+  constexpr int kC = hd / 8;                         // 16-byte chunks per row
+  constexpr int kIt = (kMK * kC + kPT - 1) / kPT;    // 1 or 2
+  uint4 kpre[kIt];
+  h8 vpre[kIt];
+  auto kv_load = [&](int k0) {
+    const int nk = min(kMK, last + 1 - k0);
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = tid + it * kPT;
+      if (e < kMK * kC) {
+        const int jk = e / kC, ck = e - jk * kC, jv = e & (kMK - 1), cv = e / kMK;
+        kpre[it] = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + (jk < nk ? jk : 0)) * hd + 8 * ck);
+        if (jk >= nk) kpre[it] = make_uint4(0u, 0u, 0u, 0u);
+        vpre[it] = *reinterpret_cast<const h8*>(V + (size_t)(k0 + (jv < nk ? jv : 0)) * hd + 8 * cv);
+        if (jv >= nk) vpre[it] = (h8){};
+      }
+    }
+  };
+  kv_load(0);
   for (int k0 = 0; k0 <= last; k0 += kMK) {
     const int nk = min(kMK, last + 1 - k0);
     const bool run = wactive && k0 <= wlast;        // the tile holds keys some row of the wave sees
     __syncthreads();                                 // the previous tile's reads are done
-    constexpr int kC = hd / 8;                       // 16-byte chunks per row
-    for (int e = tid; e < kMK * kC; e += kPT) {
-      // K: chunks of one row on neighbouring lanes; V: rows on neighbouring lanes
-      {
-        const int j = e / kC, c = e - j * kC;
-        uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + (j < nk ? j : 0)) * hd + 8 * c);
-        if (j >= nk) kv = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(&Ks[j * kQS + 8 * c]) = kv;
-      }
-      {
-        const int j = e & (kMK - 1), c = e / kMK;
-        h8 vv = *reinterpret_cast<const h8*>(V + (size_t)(k0 + (j < nk ? j : 0)) * hd + 8 * c);
-        if (j >= nk) vv = (h8){};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Vt[(8 * c + i) * kPS + j] = vv[i];
+    for (int it = 0; it < kIt; ++it) {
+      const int e = tid + it * kPT;
+      if (e < kMK * kC) {
+        const int jk = e / kC, ck = e - jk * kC, jv = e & (kMK - 1), cv = e / kMK;
+        *reinterpret_cast<uint4*>(&Ks[jk * kQS + 8 * ck]) = kpre[it];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Vt[(8 * cv + i) * kPS + jv] = vpre[it][i];
       }
     }
     __syncthreads();
+    if (k0 + kMK <= last) kv_load(k0 + kMK);         // in flight during this tile's products
     if (run) {
       f16acc sa = {};
 #pragma unroll
@@ -341,9 +367,7 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) Sw[wave][(8 * (j >> 2) + kq0 + (j & 3)) * (kMK + 1) + l32] = sa[j];
-    }
-    __syncthreads();
-    if (run) {
+      wave_sync();                                   // Sw[wave] is the wave's own
       float sc[16];
       float mx = rm;
 #pragma unroll
@@ -369,9 +393,7 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
       rl = rl * f + sum;
       rm = mx;
       if (si == 0) rfw[wave][sr] = f;
-    }
-    __syncthreads();
-    if (run) {
+      wave_sync();                                   // so are Ph, Pl and rfw[wave]
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
 #pragma unroll
