@@ -47,7 +47,11 @@ __global__ void split_kernel(const float* __restrict__ x, int ldx, __half* __res
 // CDNA4's double-rate fp16 MFMA (16 products of the inner index per
 // instruction and output element).
 //
-// Block: 4 waves, a 64 x 64 tile of C; wave (wm, wn) owns a 32 x 32 quarter.
+// Block: 4 waves, a 64 x 64 WN tile of C (64 rows of A, 64 WN rows of W,
+// WN = 1 or 2); wave (wm, wn) owns 32 x 32 WN of it, WN MFMA tiles that
+// share the A operands.  WN = 2 serves 128 outputs per A byte (A is sent
+// twice, as hi and lo) and is launched where it still gives two blocks per
+// CU.
 // K advances kGK = 64 at a time through LDS (rows padded by 8 halves); the
 // next step's tiles are loaded into registers while the current step's
 // MFMAs run.  Operand layout: lane l holds A[l % 32][8 (l / 32) + i] and
@@ -59,7 +63,7 @@ __global__ void split_kernel(const float* __restrict__ x, int ldx, __half* __res
 // Requires K % 32 == 0 and 16-byte aligned rows (lda, ldw multiples of 8);
 // a last step of 32 is zero-padded.
 // ---------------------------------------------------------------------------
-constexpr int kGT = 64;
+constexpr int kGT = 64;                  // rows (positions) per block
 constexpr int kGK = 64;
 constexpr int kGPad = kGK + 8;
 static_assert(kGPad % 8 == 0, "LDS rows must stay 16-byte aligned for the 8-half operand reads");
@@ -79,6 +83,7 @@ __device__ __forceinline__ uint4 gemm_ld(__amdgpu_buffer_rsrc_t r, unsigned off)
 // tiles[3y + 1]) of A and C (at most 64) and the weight matrix
 // w + tiles[3y + 2] * wstride, so the products of several experts over
 // their own rows of one compact A run as one launch.
+template <int WN>
 __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ahi,
                                                    const __half* __restrict__ alo, int lda,
                                                    const __half* __restrict__ w, int ldw,
@@ -87,28 +92,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
                                                    size_t wstride) {
   __shared__ __attribute__((aligned(16))) _Float16 sAh[kGT * kGPad];
   __shared__ __attribute__((aligned(16))) _Float16 sAl[kGT * kGPad];
-  __shared__ __attribute__((aligned(16))) _Float16 sW[kGT * kGPad];
+  constexpr int kGN = kGT * WN;           // output columns per block
+  __shared__ __attribute__((aligned(16))) _Float16 sW[kGN * kGPad];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int m0 = blockIdx.y * kGT;
-  const int n0 = blockIdx.x * kGT;
+  const int n0 = blockIdx.x * kGN;
   if (tiles) {
     m0 = tiles[3 * blockIdx.y];
     M = tiles[3 * blockIdx.y + 1];
     w += (size_t)tiles[3 * blockIdx.y + 2] * wstride;
   }
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32 * WN;
   // loader: row lr, 8 halves at columns lc and lc + 32 of each 64-wide step
   const int lr = tid >> 2, lc = (tid & 3) * 8;
   const __amdgpu_buffer_rsrc_t rh = gemm_rsrc(ahi, (size_t)M * lda * 2);
   const __amdgpu_buffer_rsrc_t rl = gemm_rsrc(alo, (size_t)M * lda * 2);
   const __amdgpu_buffer_rsrc_t rw = gemm_rsrc(w, (size_t)N * ldw * 2);
-  const bool am = m0 + lr < M, wnok = n0 + lr < N;
+  const bool am = m0 + lr < M, wnok = n0 + lr < N, wnok2 = WN == 2 && n0 + 64 + lr < N;
   const unsigned abase = (unsigned)((m0 + lr) * lda + lc) * 2u;
   const unsigned wbase = (unsigned)((n0 + lr) * ldw + lc) * 2u;
-  f16acc acc = {};
-  const int ar = (wm + (lane & 31)) * kGPad, br = (wn + (lane & 31)) * kGPad;
+  const unsigned wbase2 = (unsigned)((n0 + 64 + lr) * ldw + lc) * 2u;
+  f16acc acc = {}, acc2 = {};
+  const int ar = (wm + (lane & 31)) * kGPad, br = (wn + (lane & 31)) * kGPad, br2 = br + 32 * kGPad;
   const int kin = 8 * (lane >> 5);                 // the lane's inner-index offset
-  uint4 h0, h1, l0, l1, w0, w1;
+  uint4 h0, h1, l0, l1, w0, w1, v0, v1;
   auto load = [&](int k0) {
     const bool k1in = k0 + 32 < K;
     const unsigned a0 = am ? abase + (unsigned)k0 * 2u : kGOff;
@@ -121,6 +128,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
     l1 = gemm_ld(rl, a1);
     w0 = gemm_ld(rw, b0);
     w1 = gemm_ld(rw, b1);
+    if constexpr (WN == 2) {
+      v0 = gemm_ld(rw, wnok2 ? wbase2 + (unsigned)k0 * 2u : kGOff);
+      v1 = gemm_ld(rw, (wnok2 && k1in) ? wbase2 + (unsigned)(k0 + 32) * 2u : kGOff);
+    }
   };
   load(0);
   for (int k0 = 0; k0 < K; k0 += kGK) {
@@ -132,6 +143,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
     *reinterpret_cast<uint4*>(&sAl[o + 32]) = l1;
     *reinterpret_cast<uint4*>(&sW[o]) = w0;
     *reinterpret_cast<uint4*>(&sW[o + 32]) = w1;
+    if constexpr (WN == 2) {
+      *reinterpret_cast<uint4*>(&sW[o + 64 * kGPad]) = v0;
+      *reinterpret_cast<uint4*>(&sW[o + 64 * kGPad + 32]) = v1;
+    }
     __syncthreads();
     if (k0 + kGK < K) load(k0 + kGK);                // in flight during the MFMAs
 #pragma unroll
@@ -141,6 +156,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
       const h8 b = *reinterpret_cast<const h8*>(&sW[br + kk + kin]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc, 0, 0, 0);
+      if constexpr (WN == 2) {
+        const h8 b2 = *reinterpret_cast<const h8*>(&sW[br2 + kk + kin]);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b2, acc2, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b2, acc2, 0, 0, 0);
+      }
     }
   }
   const int n = n0 + wn + (lane & 31);
@@ -150,6 +170,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
     if (m < M && n < N) {
       float* p = c + (size_t)m * ldc + n;
       *p = accumulate ? *p + acc[j] : acc[j];
+    }
+    if (WN == 2 && m < M && n + 32 < N) {
+      float* p = c + (size_t)m * ldc + n + 32;
+      *p = accumulate ? *p + acc2[j] : acc2[j];
     }
   }
 }
@@ -595,9 +619,14 @@ hipError_t launch_split(const float* x, int ldx, __half* hi, __half* lo, int M, 
 
 hipError_t launch_gemm(const __half* ahi, const __half* alo, int lda, const __half* w, int ldw, float* c,
                        int ldc, int M, int N, int K, bool accumulate, hipStream_t s) {
-  const dim3 grid((N + kGT - 1) / kGT, (M + kGT - 1) / kGT);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, M, N, K,
-                     accumulate ? 1 : 0, (const int*)nullptr, (size_t)0);
+  const int rows = (M + kGT - 1) / kGT, wide = (N + 2 * kGT - 1) / (2 * kGT);
+  if (wide * rows >= 512) {                         // two 64 x 128 blocks per CU or more
+    hipLaunchKernelGGL(gemm_kernel<2>, dim3(wide, rows), dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, M,
+                       N, K, accumulate ? 1 : 0, (const int*)nullptr, (size_t)0);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3((N + kGT - 1) / kGT, rows), dim3(256), 0, s, ahi, alo, lda, w,
+                       ldw, c, ldc, M, N, K, accumulate ? 1 : 0, (const int*)nullptr, (size_t)0);
+  }
   return hipGetLastError();
 }
 hipError_t launch_gemm_grouped(const __half* ahi, const __half* alo, int lda, const __half* w, size_t wstride,
@@ -605,7 +634,7 @@ hipError_t launch_gemm_grouped(const __half* ahi, const __half* alo, int lda, co
                                hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
   const dim3 grid((N + kGT - 1) / kGT, ntiles);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, 0, N, K, 0, tiles,
+  hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, 0, N, K, 0, tiles,
                      wstride);
   return hipGetLastError();
 }
