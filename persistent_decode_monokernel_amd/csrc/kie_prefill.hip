@@ -294,7 +294,7 @@ constexpr int kPS = kMK + 8;                  // P and transposed V row stride (
 static_assert(kQS % 8 == 0 && kPS % 8 == 0, "LDS rows must stay 16-byte aligned");
 
 template <int NS>   // NS = hd / 16 inner steps of the score product
-__global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
+__global__ __launch_bounds__(kPT, 2) void attn_prefill_kernel(const float* __restrict__ QKV, int ldq,
                                                           const __half* __restrict__ kc,
                                                           const __half* __restrict__ vc, int cap, int H,
                                                           int nkv, int pos0, int T, float* __restrict__ O) {
@@ -344,28 +344,27 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
   const __half* K = kc + (size_t)g * cap * hd;
   const __half* V = vc + (size_t)g * cap * hd;
   // K/V tile staging: 16-byte chunks e = tid, tid + 256 of the tile's 32 rows;
-  // K puts a row's chunks on neighbouring lanes, V the rows.  The next tile
-  // is loaded into registers while the current one is computed.
+  // K puts a row's chunks on neighbouring lanes, V the rows.  Two register
+  // stages alternate by tile, so each tile's K/V is loaded two tiles ahead.
   constexpr int kC = hd / 8;                         // 16-byte chunks per row
   constexpr int kIt = (kMK * kC + kPT - 1) / kPT;    // 1 or 2
-  uint4 kpre[kIt];
-  h8 vpre[kIt];
-  auto kv_load = [&](int k0) {
+  uint4 kpre[2][kIt];
+  h8 vpre[2][kIt];
+  auto kv_load = [&](int r, int k0) {
     const int nk = min(kMK, last + 1 - k0);
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int e = tid + it * kPT;
       if (e < kMK * kC) {
         const int jk = e / kC, ck = e - jk * kC, jv = e & (kMK - 1), cv = e / kMK;
-        kpre[it] = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + (jk < nk ? jk : 0)) * hd + 8 * ck);
-        if (jk >= nk) kpre[it] = make_uint4(0u, 0u, 0u, 0u);
-        vpre[it] = *reinterpret_cast<const h8*>(V + (size_t)(k0 + (jv < nk ? jv : 0)) * hd + 8 * cv);
-        if (jv >= nk) vpre[it] = (h8){};
+        kpre[r][it] = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + (jk < nk ? jk : 0)) * hd + 8 * ck);
+        if (jk >= nk) kpre[r][it] = make_uint4(0u, 0u, 0u, 0u);
+        vpre[r][it] = *reinterpret_cast<const h8*>(V + (size_t)(k0 + (jv < nk ? jv : 0)) * hd + 8 * cv);
+        if (jv >= nk) vpre[r][it] = (h8){};
       }
     }
   };
-  kv_load(0);
-  for (int k0 = 0; k0 <= last; k0 += kMK) {
+  auto tile = [&](int r, int k0) {
     const int nk = min(kMK, last + 1 - k0);
     const bool run = wactive && k0 <= wlast;        // the tile holds keys some row of the wave sees
     __syncthreads();                                 // the previous tile's reads are done
@@ -374,13 +373,13 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
       const int e = tid + it * kPT;
       if (e < kMK * kC) {
         const int jk = e / kC, ck = e - jk * kC, jv = e & (kMK - 1), cv = e / kMK;
-        *reinterpret_cast<uint4*>(&Ks[jk * kQS + 8 * ck]) = kpre[it];
+        *reinterpret_cast<uint4*>(&Ks[jk * kQS + 8 * ck]) = kpre[r][it];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Vt[(8 * cv + i) * kPS + jv] = vpre[it][i];
+        for (int i = 0; i < 8; ++i) Vt[(8 * cv + i) * kPS + jv] = vpre[r][it][i];
       }
     }
     __syncthreads();
-    if (k0 + kMK <= last) kv_load(k0 + kMK);         // in flight during this tile's products
+    if (k0 + 2 * kMK <= last) kv_load(r, k0 + 2 * kMK);   // two tiles ahead
     if (run) {
       f16acc sa = {};
 #pragma unroll
@@ -435,6 +434,12 @@ __global__ __launch_bounds__(kPT) void attn_prefill_kernel(const float* __restri
         }
       }
     }
+  };
+  kv_load(0, 0);
+  if (kMK <= last) kv_load(1, kMK);
+  for (int k0 = 0; k0 <= last; k0 += 2 * kMK) {
+    tile(0, k0);
+    if (k0 + kMK <= last) tile(1, k0 + kMK);
   }
   // the row sums, from the softmax lanes to the accumulator lanes
   __syncthreads();
