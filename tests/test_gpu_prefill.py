@@ -61,6 +61,10 @@ PREFILL_CASES = {
     # name: (workload, overrides, decode steps)
     "tiny": ("tiny", {}, 64),
     "gqa2_narrow": ("tiny", dict(n_heads=8, n_kv_heads=4, head_dim=32, prompt_len=80), 16),
+    # head sizes whose value columns only partly fill their last 32-wide tile (16, 48, 112)
+    "hd16_gqa2": ("tiny", dict(n_heads=8, n_kv_heads=4, head_dim=16, prompt_len=150), 16),
+    "hd48_gqa2": ("tiny", dict(n_heads=4, n_kv_heads=2, head_dim=48, prompt_len=150), 16),
+    "hd112": ("tiny", dict(n_heads=4, n_kv_heads=4, head_dim=112, prompt_len=150), 16),
     # grouped-query attention 32 x 80 over 8 KV heads, a 1200-position prompt
     "longctx_2l_1200": ("longctx", dict(n_layers=2, prompt_len=1200), 8),
     # a full first chunk of 2048 positions, then a ragged second one
