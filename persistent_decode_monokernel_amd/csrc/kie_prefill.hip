@@ -638,9 +638,14 @@ hipError_t launch_gemm_grouped(const __half* ahi, const __half* alo, int lda, co
                                int ldw, float* c, int ldc, const int* tiles, int ntiles, int N, int K,
                                hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
-  const dim3 grid((N + kGT - 1) / kGT, ntiles);
-  hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, 0, N, K, 0, tiles,
-                     wstride);
+  const int wide = (N + 2 * kGT - 1) / (2 * kGT);
+  if (wide * ntiles >= 512) {                       // two 64 x 128 blocks per CU or more
+    hipLaunchKernelGGL(gemm_kernel<2>, dim3(wide, ntiles), dim3(256), 0, s, ahi, alo, lda, w, ldw, c, ldc, 0, N,
+                       K, 0, tiles, wstride);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3((N + kGT - 1) / kGT, ntiles), dim3(256), 0, s, ahi, alo, lda, w,
+                       ldw, c, ldc, 0, N, K, 0, tiles, wstride);
+  }
   return hipGetLastError();
 }
 
