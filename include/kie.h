@@ -236,8 +236,10 @@ int kie_debug_gemv(const void *w, const float *x, float *y, int32_t rows, int32_
 
 /* c = a w^T (or c += a w^T with accumulate != 0) with the batched
  * prefill's matrix-core product: w device fp16 [n][k] row-major, a device
- * fp32 [m][k], c device fp32 [m][n]; k a positive multiple of 32.  Allocates
- * and frees a 4 m k byte workspace.  Synchronous on `hip_stream`. */
+ * fp32 [m][k], c device fp32 [m][n]; k a positive multiple of 32; m, n, k at
+ * most 65536, and n k and m k each under 2^30 elements (the kernel's byte
+ * offsets are 32-bit), else KIE_ERR_INVALID_ARG.  Allocates and frees a
+ * 4 m k byte workspace.  Synchronous on `hip_stream`. */
 int kie_debug_gemm(const void *w, const float *a, float *c, int32_t m, int32_t n, int32_t k,
                    int32_t accumulate, void *hip_stream);
 

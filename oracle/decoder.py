@@ -320,18 +320,57 @@ class Oracle:
             X = X + O.reshape(n, H * hd) @ self.lw(l, "wo").T
             Hn = rmsnorm(X, self.w["layers"][l]["ffn_norm"], eps)
             if c.is_moe:
-                Y = np.empty_like(X)
-                for p in range(n):
-                    r = []
-                    Y[p], sel = self._ffn(l, Hn[p], r)
-                    ids, rl = self.route.get(p, ([], []))
-                    self.route[p] = (list(ids) + [np.asarray(sel, np.int32)], list(rl) + r)
+                Y = self._moe_prompt(l, Hn)
             else:
                 Y = swiglu(Hn, self.lw(l, "w_gate"), self.lw(l, "w_up"), self.lw(l, "w_down"))
             X = X + Y
         for p in list(self.route):
             ids, rl = self.route[p]
             self.route[p] = (np.stack(ids), np.stack(rl))
+
+    def _moe_prompt(self, l: int, Hn: np.ndarray) -> np.ndarray:
+        """The mixture-of-experts FFN of layer ``l`` for every prompt position.
+
+        Each position is routed exactly as :func:`moe_ffn` routes one token
+        (its own router matrix-vector product, softmax, top-k).  Each expert's
+        SwiGLU is then applied to all the positions that use it as one matrix
+        product (the same formula, row by row), and position p sums its
+        experts in :func:`moe_ffn`'s order: shared experts, then the routed
+        ones by rank.  Appends the routing to ``self.route``."""
+        c = self.cfg
+        n = Hn.shape[0]
+        E, S = c.n_experts, c.n_shared_experts
+        renorm = getattr(c, "moe_renorm", False)
+        router = self.lw(l, "router")
+        sel_all, w_all = [], []
+        users = [[] for _ in range(E + S)]
+        for p in range(n):
+            r = router @ Hn[p]
+            pi, sel = moe_route(r, c.top_k)
+            w = pi / pi[sel].sum() if renorm else pi
+            sel_all.append(sel)
+            w_all.append(w)
+            for e in sel:
+                users[int(e)].append(p)
+            ids, rl = self.route.get(p, ([], []))
+            self.route[p] = (list(ids) + [np.asarray(sel, np.int32)], list(rl) + [r])
+        for s in range(S):
+            users[E + s] = list(range(n))
+        out = [None] * (E + S)                # expert e -> {position: SwiGLU_e(h_p)}
+        for e in range(E + S):
+            if users[e]:
+                g, u, d = self.expert(l, e)
+                rows = np.asarray(users[e])
+                out[e] = dict(zip(users[e], swiglu(Hn[rows], g, u, d)))
+        Y = np.zeros_like(Hn)
+        for p in range(n):
+            y = Y[p]
+            for s in range(S):
+                y = y + out[E + s][p]
+            for e in sel_all[p]:
+                y = y + w_all[p][e] * out[int(e)][p]
+            Y[p] = y
+        return Y
 
     # -- generation -------------------------------------------------------------
     def decode(self, n: int, force: Optional[Sequence[int]] = None, keep_logits: bool = True):

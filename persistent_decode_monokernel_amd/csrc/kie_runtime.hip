@@ -669,6 +669,9 @@ int kie_debug_gemm(const void* w, const float* a, float* c, int32_t m, int32_t n
   g_err.clear();
   if (m < 1 || n < 1 || k < 32 || k % 32 != 0 || m > 65536 || n > 65536 || k > 65536)
     return fail(KIE_ERR_INVALID_ARG, "need m, n >= 1 and k a positive multiple of 32 (all <= 65536)");
+  // the product kernel addresses each operand with 32-bit byte offsets
+  if ((size_t)n * k * sizeof(__half) >= ((size_t)1 << 31) || (size_t)m * k * sizeof(__half) >= ((size_t)1 << 31))
+    return fail(KIE_ERR_INVALID_ARG, "w (n x k) and the split a (m x k) must each be under 2 GiB of fp16");
   int rc;
   if ((rc = check_device_range(w, (size_t)n * k * sizeof(__half), "w"))) return rc;
   if ((rc = check_device_range(a, (size_t)m * k * sizeof(float), "a"))) return rc;

@@ -117,6 +117,10 @@ def test_batched_prefill_and_gemm_validate_arguments_on_the_host():
     for m, n, k in ((0, 64, 32), (4, 0, 32), (4, 64, 0), (4, 64, 48), (4, 64, 70000)):
         assert lib.kie_debug_gemm(None, None, None, m, n, k, 0, None) == -1, (m, n, k)
         assert "multiple of 32" in lib.kie_last_error().decode()
+    # 32768 x 32768 fp16 is 2 GiB: past the product kernel's 32-bit offsets
+    for m, n, k in ((4, 32768, 32768), (65536, 64, 16384 * 2)):
+        assert lib.kie_debug_gemm(None, None, None, m, n, k, 0, None) == -1, (m, n, k)
+        assert "2 GiB" in lib.kie_last_error().decode()
 
 
 def test_moe_renorm_flag_is_accepted():

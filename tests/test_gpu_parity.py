@@ -209,26 +209,77 @@ def test_tiny_weights_too_small_rejected(torch, kie):
 
 
 # ------------------------------------------------------ end-to-end, 2.2B
-def test_2b_full_size_parity_sampled(torch, kie):
-    """The ~2.2B model at full size and in the launch shape the benchmark
-    times: prompt 512, then decode; the first 6 steps are replayed by the
-    oracle (teacher forced), and every layer's K/V rows at sampled
-    positions are checked."""
+@pytest.mark.timeout(900)
+def test_2b_full_replay(torch, kie):
+    """The ~2.2B model at full size in the launch the benchmark times:
+    prompt 512, then 512 greedy decode steps in ONE kie_decode call (positions
+    511..1022, where the context-sized split count grows from 4 to 8 per KV
+    head).  The oracle replays every step teacher-forced on the kernel's
+    tokens; every step is held to the logit and token bar, and K/V rows of
+    three layers are checked at positions across the prompt and the decode."""
     cfg = _model("2b")
-    _say("2b parity: weights")
+    _say("2b full replay: weights")
     W = _gpu_weights(torch, cfg)
     prompt = make_prompt(cfg)
-    n = 6
-    _say("2b parity: gpu run")
+    n = cfg.n_decode
+    _say("2b full replay: gpu run")
     eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n)
-    _say("2b parity: oracle replay")
+    assert eng.position == len(prompt) - 1 + n
+    _say("2b full replay: oracle replay of", n, "steps")
     Wn = weights_to_numpy(W)
     o, zo = _oracle_replay(cfg, Wn, prompt, toks)
     rep = compare_steps(z, toks, zo)
-    _say("2b", rep)
+    _say("2b full replay", rep)
+    assert rep["pinned"] >= n // 2
     P = len(prompt)
     _check_kv(eng, o, (0, 12, 24),
-              [(0, 1), (255, 256), (P - 2, P - 1), (P - 1 + n - 1, P - 1 + n)])
+              [(0, 1), (255, 256), (P - 2, P - 1), (600, 601), (800, 801), (P - 1 + n - 2, P - 1 + n)])
+    eng.close()
+
+
+def test_occupancy_is_checked_at_create(torch, kie):
+    """A grid that cannot be co-resident is refused by kie_create, before
+    any launch (4096 workgroups of one per compute unit on 256 units)."""
+    cfg = _model("tiny")
+    W = _gpu_weights(torch, cfg)
+    with pytest.raises(kie.KieError) as ei:
+        kie.Engine(cfg, W, n_workgroups=4096)
+    assert ei.value.status == "KIE_ERR_OCCUPANCY"
+
+
+def test_argmax_exact_ties_pick_the_lowest_index(torch, kie):
+    """Rows of lm_head that are bit-identical give bit-identical logits, so
+    the greedy token faces exact ties.  Rows 7 and 3001 hold +8 r and rows 9
+    and 2000 hold -8 r for a random row r, every other row is zero: each step
+    the maximum is shared by two rows (7 and 3001 when r.h > 0, else 9 and
+    2000) and the token must be the lower of the two.  Then every lm_head row
+    equal: all logits tie and the token must be 0 at every step."""
+    cfg = _model("tiny")
+    _say("argmax ties")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    r = W["lm_head"][5].float()
+    lm = torch.zeros_like(W["lm_head"])
+    lm[7] = lm[3001] = (8.0 * r).half()
+    lm[9] = lm[2000] = (-8.0 * r).half()
+    W2 = dict(W)
+    W2["lm_head"] = lm.contiguous()
+    n = 16
+    eng, toks, z = _run_gpu(torch, kie, cfg, W2, prompt, n)
+    for i in range(n):
+        assert z[i][7] == z[i][3001] and z[i][9] == z[i][2000], i
+        want = 7 if z[i][7] > 0 else 9
+        assert z[i][want] == z[i].max()
+        assert toks[i] == want, (i, toks[i], want)
+    # the logits themselves against the oracle (tied steps are unpinned)
+    o, zo = _oracle_replay(cfg, weights_to_numpy(W2), prompt, toks)
+    compare_steps(z, toks, zo)
+    eng.close()
+    W3 = dict(W)
+    W3["lm_head"] = W["lm_head"][11:12].expand_as(W["lm_head"]).contiguous()
+    eng, toks, z = _run_gpu(torch, kie, cfg, W3, prompt, n)
+    assert np.all(z == z[:, :1]), "identical rows must give identical logits"
+    np.testing.assert_array_equal(toks, np.zeros(n, np.int32))
     eng.close()
 
 
@@ -372,4 +423,31 @@ def test_full_size_variant_parity_sampled(torch, kie, name, prompt_len, n, layer
     rep = compare_steps(z, toks, zo, skip=[q - (P - 1) for q in tied if q >= P - 1])
     _say(name, rep, "routing near-ties at positions", tied)
     _check_kv(eng, o, layers, [(0, 1), (P // 2, P // 2 + 1), (P - 1, P - 1 + n)], exclude=tied)
+    eng.close()
+
+
+@pytest.mark.timeout(900)
+def test_moe_full_depth_prompt_512(torch, kie):
+    """The MoE workload at full depth and width with its real prompt of 512
+    tokens, then 128 decode steps; the oracle replays all of them (the first
+    128 decode steps of the 512-step run).  Routing is compared at every
+    prompt and decode position."""
+    cfg = _model("moe")
+    n = 128
+    cap = cfg.prompt_len + cfg.n_decode
+    _say("moe full depth 512: weights")
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    _say("moe full depth 512: gpu run")
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n, max_seq=cap)
+    _say("moe full depth 512: oracle replay")
+    o = Oracle(cfg.with_(max_seq=cap), weights_to_numpy(W), cache_bytes=96 << 30, kv_fp16=True)
+    o.prefill(prompt)
+    _, zo = o.decode(n, force=toks)
+    P = len(prompt)
+    tied = _moe_check(eng, o, cfg, range(P - 1 + n))
+    rep = compare_steps(z, toks, zo, skip=[q - (P - 1) for q in tied if q >= P - 1])
+    _say("moe full depth 512", rep, "routing near-ties at positions", tied)
+    assert rep["pinned"] >= n // 2
+    _check_kv(eng, o, (0, 11, 23), [(0, 1), (P // 2, P // 2 + 1), (P - 1, P - 1 + n)], exclude=tied)
     eng.close()

@@ -101,3 +101,24 @@ def test_planted_gqa_index_mistake_is_caught(monkeypatch):
     _, z = o.decode(1)
     want = brute.last_logits(cfg, W, list(prompt))
     assert not np.allclose(z[0], want, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("name", ["wq", "wo"])
+def test_planted_transposed_operand_is_caught(name):
+    # a square projection (d_model == n_heads * head_dim in the small
+    # workload) applied transposed still runs, so only the pins can catch it
+    cfg = SMALL_GQA
+    W = weights_to_numpy(make_weights(cfg, seed=3, std=0.3))
+    prompt = make_prompt(cfg, seed=1)
+    assert W["layers"][0][name].shape[0] == W["layers"][0][name].shape[1]
+
+    class Transposed(dec.Oracle):
+        def lw(self, l, nm):
+            w = super().lw(l, nm)
+            return w.T if nm == name else w
+
+    o = Transposed(cfg, W, dtype=np.float64)
+    o.prefill(prompt)
+    _, z = o.decode(1)
+    want = brute.last_logits(cfg, W, list(prompt))
+    assert not np.allclose(z[0], want, rtol=1e-6, atol=1e-8), name

@@ -300,6 +300,11 @@ def test_moe_routing_record_is_per_position_and_prefill_independent():
         np.testing.assert_array_equal(a.route[p][0], b.route[p][0])
         np.testing.assert_allclose(a.route[p][1], b.route[p][1], atol=1e-5)
         assert a.route[p][0].shape == (cfg.n_layers, cfg.top_k)
+    for l in range(cfg.n_layers):
+        np.testing.assert_allclose(a.K[l][:, :P - 1], b.K[l][:, :P - 1], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(a.V[l][:, :P - 1], b.V[l][:, :P - 1], atol=1e-5, rtol=1e-5)
+    np.testing.assert_allclose(a.decode(2)[1], b.decode(2)[1], atol=1e-5, rtol=1e-5)
+    a.reset(); a.prefill(prompt, batched=True)
     a.decode(3)
     assert sorted(a.route) == list(range(P + 2))
     for i in range(3):
