@@ -163,14 +163,18 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * the positions by expert on the host and run each expert's products over
  * its rows.  Needs d_model, n_heads * head_dim and ffn_hidden (MoE:
  * expert_hidden) to be multiples of 32 and head_dim a multiple of 16;
- * otherwise KIE_ERR_UNSUPPORTED (use kie_prefill).  Allocates a workspace
- * for the call and frees it before returning: 4 T (d + 2 qd + 2 kd + 2 F
- * + max(d, qd, F)) bytes, with qd = n_heads head_dim, kd = n_kv_heads
- * head_dim, F = ffn_hidden (0 for MoE, which adds its routing and
- * per-expert buffers) and T = min(2048, n_tokens - 1) positions per
- * chunk.  A prompt's positions are all known up front, so its products are
- * dense matrix products; decode steps stay on the GEMV path of the
- * persistent kernel. */
+ * otherwise KIE_ERR_UNSUPPORTED (use kie_prefill).  Its device workspace
+ * belongs to the handle: allocated by the first call that needs more than
+ * the handle holds, kept for later calls and freed by kie_destroy.  It
+ * takes about 4 T (d + 2 qd + 2 kd + 2 F + max(d, qd, F)) bytes, with qd =
+ * n_heads head_dim, kd = n_kv_heads head_dim, F = ffn_hidden (0 for MoE,
+ * which adds its routing and per-expert buffers) and T = min(2048,
+ * n_tokens - 1) positions per chunk.  A prompt's positions are all known
+ * up front, so its products are dense matrix products; decode steps stay
+ * on the GEMV path of the persistent kernel.  Cited: "Breaking the memory
+ * wall: 3,000 tokens/s inference on standard GPUs", section "1. The
+ * Monokernel Runtime" (the decode path; the prompt's own pass is not
+ * described there). */
 int kie_prefill_batched(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
 /* Generates n_steps tokens in one launch.  out_tokens: device int32

@@ -80,6 +80,11 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 }  // namespace
 
+namespace {
+constexpr int kPrefillChunk = 2048;                // positions per batched prefill chunk, at most
+size_t moe_max_tiles(size_t rows, int E);
+}  // namespace
+
 struct kie_handle {
   kie_config cfg{};
   kie::Params base{};            // shapes, weights and owned buffers (per-call fields unset)
@@ -101,6 +106,11 @@ struct kie_handle {
   int last_decode_steps = 0;
   int trace_events = 0;          // events per workgroup recorded by the last decode
   unsigned epoch_next = 1;       // first activation epoch of the next launch
+  void* pf_ws = nullptr;         // batched prefill workspace (grown on demand, freed with the handle)
+  size_t pf_ws_bytes = 0;
+  // MoE batched prefill: host copies of one chunk's routing and grouping,
+  // sized at creation for the largest chunk
+  std::vector<int> moe_ids, moe_perm, moe_inv, moe_tiles, moe_off, moe_fill;
 };
 
 namespace {
@@ -120,6 +130,7 @@ void free_handle(kie_handle* h) {
   if (!h) return;
   (void)hipStreamSynchronize(h->stream);
   for (void* p : h->allocs) (void)hipFree(p);
+  if (h->pf_ws) (void)hipFree(h->pf_ws);
   if (h->ev0) (void)hipEventDestroy(h->ev0);
   if (h->ev1) (void)hipEventDestroy(h->ev1);
   delete h;
@@ -423,6 +434,16 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
     return bail(fail(KIE_ERR_HIP, "initialising handle buffers failed"));
   const int tmo = c.timeout_ms > 0 ? c.timeout_ms : 20000;
   p.timeout_ticks = (long long)tmo * h->ticks_per_ms;
+  if (c.n_experts) {
+    // host side of the batched prefill's routing, for its largest chunk
+    const size_t rk = (size_t)std::max(1, std::min(kPrefillChunk, c.max_seq)) * c.top_k;
+    h->moe_ids.resize(rk);
+    h->moe_perm.resize(rk);
+    h->moe_inv.resize(rk);
+    h->moe_tiles.resize(3 * moe_max_tiles(rk, c.n_experts));
+    h->moe_off.resize(c.n_experts + 1);
+    h->moe_fill.resize(c.n_experts);
+  }
   *out = h;
   g_err.clear();
   return KIE_OK;
@@ -460,7 +481,6 @@ int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logit
 // Per chunk and layer: RMSNorm -> Q/K/V products -> RoPE + fp16 K/V rows into
 // the cache -> causal attention over the cache -> O product + residual ->
 // RMSNorm -> gate/up products -> SwiGLU -> down product + residual.
-constexpr int kPrefillChunk = 2048;
 
 // Mixture-of-experts FFN of one chunk and layer (hi/lo hold the normed
 // input): router product, routing per position, positions grouped by expert
@@ -471,7 +491,7 @@ struct MoeWs {
   float *R, *wts, *Gc, *Uc, *Yc;
   int *ids, *perm, *inv, *tiles;
   __half *ch, *cl, *sh, *sl;
-  std::vector<int> h_ids, h_perm, h_inv, h_tiles, off;
+  int *h_ids, *h_perm, *h_inv, *h_tiles, *off, *fill;   // host, owned by the handle
 };
 
 // Row tiles of the grouped products: at most rows / 64 + E of them.
@@ -488,15 +508,15 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
   int rc;
   if ((rc = ok(kie::launch_gemm(hi, lo, d, w.router, d, m.R, E, Tn, E, d, false, s)))) return rc;
   if ((rc = ok(kie::launch_route(m.R, E, k, p.moe_renorm, m.ids, m.wts, p.expert_log, p.L, l, c0, Tn, s)))) return rc;
-  KIE_HIP(hipMemcpyAsync(m.h_ids.data(), m.ids, sizeof(int) * rows, hipMemcpyDeviceToHost, s));
+  KIE_HIP(hipMemcpyAsync(m.h_ids, m.ids, sizeof(int) * rows, hipMemcpyDeviceToHost, s));
   KIE_HIP(hipStreamSynchronize(s));
   // compact rows ordered by expert, then position: perm[q] = t * k + a
-  std::fill(m.off.begin(), m.off.end(), 0);
+  std::fill(m.off, m.off + E + 1, 0);
   for (int i = 0; i < rows; ++i) ++m.off[m.h_ids[i] + 1];
   for (int e = 0; e < E; ++e) m.off[e + 1] += m.off[e];
-  std::vector<int> fill(m.off.begin(), m.off.end() - 1);
+  std::copy(m.off, m.off + E, m.fill);
   for (int i = 0; i < rows; ++i) {
-    const int q = fill[m.h_ids[i]]++;
+    const int q = m.fill[m.h_ids[i]]++;
     m.h_perm[q] = i;
     m.h_inv[i] = q;
   }
@@ -508,9 +528,9 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
       m.h_tiles[3 * nt + 1] = std::min(r0 + 64, m.off[e + 1]);
       m.h_tiles[3 * nt + 2] = e;
     }
-  KIE_HIP(hipMemcpyAsync(m.perm, m.h_perm.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
-  KIE_HIP(hipMemcpyAsync(m.inv, m.h_inv.data(), sizeof(int) * rows, hipMemcpyHostToDevice, s));
-  KIE_HIP(hipMemcpyAsync(m.tiles, m.h_tiles.data(), sizeof(int) * 3 * nt, hipMemcpyHostToDevice, s));
+  KIE_HIP(hipMemcpyAsync(m.perm, m.h_perm, sizeof(int) * rows, hipMemcpyHostToDevice, s));
+  KIE_HIP(hipMemcpyAsync(m.inv, m.h_inv, sizeof(int) * rows, hipMemcpyHostToDevice, s));
+  KIE_HIP(hipMemcpyAsync(m.tiles, m.h_tiles, sizeof(int) * 3 * nt, hipMemcpyHostToDevice, s));
   if ((rc = ok(kie::launch_gather_rows(hi, lo, d, m.perm, k, m.ch, m.cl, rows, s)))) return rc;
   const size_t gate_e = (size_t)Fe * d, down_e = (size_t)d * Fe;
   if ((rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_gate, gate_e, d, m.Gc, Fe, m.tiles, nt, Fe, d, s))) ||
@@ -529,66 +549,103 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
   return ok(kie::launch_combine(X, d, m.Yc, m.inv, k, Tn, s));
 }
 
-int prefill_batched(kie_handle* h, int n) {
-  const kie::Params& p = h->base;
-  const int T = std::max(1, std::min(kPrefillChunk, n - 1));   // positions per chunk (workspace rows)
+// The batched prefill's device workspace for chunks of T positions: the
+// chunk's activations (fp32), the hi/lo fp16 split of the widest product
+// input and, for MoE, the routing and grouped-row buffers.  Returns its size
+// in bytes; with a base address, also carves it (regions 256-byte aligned).
+struct PfWs {
+  float *X, *QKV, *O, *G, *U;
+  __half *hi, *lo;
+  MoeWs m;
+};
+
+size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
   const bool moe = p.E != 0;
   const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
   const int wide = std::max(std::max(d, qd), F);
-  const size_t fbytes = sizeof(float) * (size_t)T * ((size_t)d + qkv + qd + 2 * (size_t)F);
-  const size_t hbytes = sizeof(__half) * (size_t)T * wide * 2;
-  // MoE: router logits, routing, compact rows (T * top_k of them), the row
-  // tiles of the grouped products; each region starts 256-byte aligned
-  const size_t rk = (size_t)T * (moe ? p.topk : 0), rx = std::max(rk, (size_t)T);
-  const size_t mbase = (fbytes + hbytes + 255) & ~(size_t)255;
-  size_t mo[13] = {}, mbytes = 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return base ? base + at : nullptr;
+  };
+  const size_t t = (size_t)T;
+  char* X = take(sizeof(float) * t * d);
+  char* QKV = take(sizeof(float) * t * qkv);
+  char* O = take(sizeof(float) * t * qd);
+  char* G = take(sizeof(float) * t * F);
+  char* U = take(sizeof(float) * t * F);
+  char* hi = take(sizeof(__half) * t * wide);
+  char* lo = take(sizeof(__half) * t * wide);
+  if (w) {
+    w->X = reinterpret_cast<float*>(X);
+    w->QKV = reinterpret_cast<float*>(QKV);
+    w->O = reinterpret_cast<float*>(O);
+    w->G = reinterpret_cast<float*>(G);
+    w->U = reinterpret_cast<float*>(U);
+    w->hi = reinterpret_cast<__half*>(hi);
+    w->lo = reinterpret_cast<__half*>(lo);
+  }
   if (moe) {
-    const size_t Fe = p.Fe, rows_d = rk * d, ntile = moe_max_tiles(rk, p.E);
-    const size_t sz[13] = {sizeof(float) * (size_t)T * p.E, sizeof(float) * rk,   // R, wts
-                           sizeof(float) * rx * Fe, sizeof(float) * rx * Fe,      // Gc, Uc
-                           sizeof(float) * rows_d,                                // Yc
-                           sizeof(int) * rk, sizeof(int) * rk, sizeof(int) * rk,  // ids, perm, inv
-                           sizeof(int) * 3 * ntile,                               // tiles
-                           sizeof(__half) * rows_d, sizeof(__half) * rows_d,      // ch, cl
-                           sizeof(__half) * rx * Fe, sizeof(__half) * rx * Fe};   // sh, sl
-    for (int i = 0; i < 13; ++i) {
-      mo[i] = mbytes;
-      mbytes += (sz[i] + 255) & ~(size_t)255;
+    // router logits, routing, compact rows (T * top_k of them), row tiles
+    const size_t rk = t * p.topk, rx = std::max(rk, t), Fe = p.Fe, rows_d = rk * d;
+    char* R = take(sizeof(float) * t * p.E);
+    char* wts = take(sizeof(float) * rk);
+    char* Gc = take(sizeof(float) * rx * Fe);
+    char* Uc = take(sizeof(float) * rx * Fe);
+    char* Yc = take(sizeof(float) * rows_d);
+    char* ids = take(sizeof(int) * rk);
+    char* perm = take(sizeof(int) * rk);
+    char* inv = take(sizeof(int) * rk);
+    char* tiles = take(sizeof(int) * 3 * moe_max_tiles(rk, p.E));
+    char* ch = take(sizeof(__half) * rows_d);
+    char* cl = take(sizeof(__half) * rows_d);
+    char* sh = take(sizeof(__half) * rx * Fe);
+    char* sl = take(sizeof(__half) * rx * Fe);
+    if (w) {
+      MoeWs& m = w->m;
+      m.R = reinterpret_cast<float*>(R);
+      m.wts = reinterpret_cast<float*>(wts);
+      m.Gc = reinterpret_cast<float*>(Gc);
+      m.Uc = reinterpret_cast<float*>(Uc);
+      m.Yc = reinterpret_cast<float*>(Yc);
+      m.ids = reinterpret_cast<int*>(ids);
+      m.perm = reinterpret_cast<int*>(perm);
+      m.inv = reinterpret_cast<int*>(inv);
+      m.tiles = reinterpret_cast<int*>(tiles);
+      m.ch = reinterpret_cast<__half*>(ch);
+      m.cl = reinterpret_cast<__half*>(cl);
+      m.sh = reinterpret_cast<__half*>(sh);
+      m.sl = reinterpret_cast<__half*>(sl);
     }
   }
-  void* ws = nullptr;
-  hipError_t e = hipMalloc(&ws, mbase + mbytes);
-  if (e != hipSuccess)
-    return fail(KIE_ERR_HIP, std::string("prefill workspace hipMalloc failed: ") + hipGetErrorString(e));
-  MoeWs mw{};
+  return off;
+}
+
+// Prefill of positions 0 .. n - 2 in chunks of T positions, with the
+// workspace `ws` carved for T (prefill_ws).  No allocation.
+int prefill_batched(kie_handle* h, int n, int T, char* ws) {
+  const kie::Params& p = h->base;
+  const bool moe = p.E != 0;
+  const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
+  PfWs W{};
+  (void)prefill_ws(p, T, ws, &W);
+  MoeWs& mw = W.m;
   if (moe) {
-    char* b = static_cast<char*>(ws) + mbase;
-    mw.R = reinterpret_cast<float*>(b + mo[0]);
-    mw.wts = reinterpret_cast<float*>(b + mo[1]);
-    mw.Gc = reinterpret_cast<float*>(b + mo[2]);
-    mw.Uc = reinterpret_cast<float*>(b + mo[3]);
-    mw.Yc = reinterpret_cast<float*>(b + mo[4]);
-    mw.ids = reinterpret_cast<int*>(b + mo[5]);
-    mw.perm = reinterpret_cast<int*>(b + mo[6]);
-    mw.inv = reinterpret_cast<int*>(b + mo[7]);
-    mw.tiles = reinterpret_cast<int*>(b + mo[8]);
-    mw.ch = reinterpret_cast<__half*>(b + mo[9]);
-    mw.cl = reinterpret_cast<__half*>(b + mo[10]);
-    mw.sh = reinterpret_cast<__half*>(b + mo[11]);
-    mw.sl = reinterpret_cast<__half*>(b + mo[12]);
-    mw.h_ids.resize(rk);
-    mw.h_perm.resize(rk);
-    mw.h_inv.resize(rk);
-    mw.h_tiles.resize(3 * moe_max_tiles(rk, p.E));
-    mw.off.resize(p.E + 1);
+    mw.h_ids = h->moe_ids.data();
+    mw.h_perm = h->moe_perm.data();
+    mw.h_inv = h->moe_inv.data();
+    mw.h_tiles = h->moe_tiles.data();
+    mw.off = h->moe_off.data();
+    mw.fill = h->moe_fill.data();
   }
-  float* X = static_cast<float*>(ws);
-  float* QKV = X + (size_t)T * d;
-  float* O = QKV + (size_t)T * qkv;
-  float* G = O + (size_t)T * qd;
-  float* U = G + (size_t)T * F;
-  __half* hi = reinterpret_cast<__half*>(U + (size_t)T * F);
-  __half* lo = hi + (size_t)T * wide;
+  float* X = W.X;
+  float* QKV = W.QKV;
+  float* O = W.O;
+  float* G = W.G;
+  float* U = W.U;
+  __half* hi = W.hi;
+  __half* lo = W.lo;
   hipStream_t s = h->stream;
   const size_t layer_kv = (size_t)p.nkv * p.cap * p.hd;
   int rc = KIE_OK;
@@ -624,16 +681,14 @@ int prefill_batched(kie_handle* h, int n) {
       }
     }
   }
-  e = hipStreamSynchronize(s);
+  const hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess && rc == KIE_OK)
     rc = fail(KIE_ERR_HIP, std::string("prefill failed: ") + hipGetErrorString(e));
-  (void)hipFree(ws);
   return rc;
 }
-}  // namespace
 
-int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
-  g_err.clear();
+// Validation shared by both batched prefill entries (nothing launched).
+int prefill_batched_check(kie_handle* h, const int32_t* tokens, int32_t n) {
   if (!h || !tokens) return fail(KIE_ERR_INVALID_ARG, "handle or tokens is NULL");
   if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
   if (h->pos != 0 || h->pending) return fail(KIE_ERR_BAD_STATE, "prefill needs a fresh or reset handle");
@@ -646,9 +701,15 @@ int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
   for (int i = 0; i < n; ++i)
     if (tokens[i] < 0 || tokens[i] >= h->cfg.vocab_in)
       return fail(KIE_ERR_TOKEN_RANGE, "prompt token " + std::to_string(i) + " out of range");
+  return KIE_OK;
+}
+
+// Runs a validated batched prefill with chunks of T positions in workspace
+// `ws` and makes the last prompt token pending.
+int prefill_batched_run(kie_handle* h, const int32_t* tokens, int32_t n, int T, char* ws) {
   KIE_HIP(hipMemcpyAsync(h->d_prompt, tokens, sizeof(int) * n, hipMemcpyHostToDevice, h->stream));
   KIE_HIP(hipEventRecord(h->ev0, h->stream));
-  int rc = prefill_batched(h, n);
+  int rc = prefill_batched(h, n, T, ws);
   if (rc) {
     h->broken = true;
     return rc;
@@ -662,6 +723,30 @@ int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
   h->pos = n - 1;
   h->pending = true;
   return KIE_OK;
+}
+
+}  // namespace
+
+int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
+  g_err.clear();
+  int rc = prefill_batched_check(h, tokens, n);
+  if (rc) return rc;
+  const int T = std::max(1, std::min(kPrefillChunk, n - 1));   // positions per chunk (workspace rows)
+  const size_t need = prefill_ws(h->base, T, nullptr, nullptr);
+  if (need > h->pf_ws_bytes) {
+    // grow the handle's workspace; the stream is idle between calls
+    KIE_HIP(hipStreamSynchronize(h->stream));
+    if (h->pf_ws) (void)hipFree(h->pf_ws);
+    h->pf_ws = nullptr;
+    h->pf_ws_bytes = 0;
+    void* ws = nullptr;
+    const hipError_t e = hipMalloc(&ws, need);
+    if (e != hipSuccess)
+      return fail(KIE_ERR_HIP, std::string("prefill workspace hipMalloc failed: ") + hipGetErrorString(e));
+    h->pf_ws = ws;
+    h->pf_ws_bytes = need;
+  }
+  return prefill_batched_run(h, tokens, n, T, static_cast<char*>(h->pf_ws));
 }
 
 int kie_debug_gemm(const void* w, const float* a, float* c, int32_t m, int32_t n, int32_t k,

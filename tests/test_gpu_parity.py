@@ -239,11 +239,15 @@ def test_2b_full_replay(torch, kie):
 
 def test_occupancy_is_checked_at_create(torch, kie):
     """A grid that cannot be co-resident is refused by kie_create, before
-    any launch (4096 workgroups of one per compute unit on 256 units)."""
+    any launch: the decode kernel fits one workgroup per compute unit, so 32
+    more workgroups than compute units must fail with KIE_ERR_OCCUPANCY
+    (a far larger grid fails earlier, on the LDS its attention splits
+    need)."""
     cfg = _model("tiny")
     W = _gpu_weights(torch, cfg)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     with pytest.raises(kie.KieError) as ei:
-        kie.Engine(cfg, W, n_workgroups=4096)
+        kie.Engine(cfg, W, n_workgroups=n_cu + 32)
     assert ei.value.status == "KIE_ERR_OCCUPANCY"
 
 
