@@ -177,6 +177,22 @@ int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
  * described there). */
 int kie_prefill_batched(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  As
+ * kie_prefill_batched (same arguments, the same K/V rows and pending token
+ * bit for bit, the same errors), but its workspace is a static device array
+ * of KIE_PREFILL_SCRATCH_MIB MiB, which the library holds on every GPU it
+ * runs on until the process ends, and it calls no hipMalloc or hipFree.
+ * When the usual chunk's workspace (see kie_prefill_batched) exceeds the
+ * array, the prompt goes through in smaller chunks; KIE_ERR_UNSUPPORTED if
+ * one position's workspace exceeds it.  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that overlap on
+ * one GPU (other threads, other handles' streams) race and must be
+ * serialised by the caller.  The handle's device must be current
+ * (KIE_ERR_BAD_STATE otherwise). */
+#define KIE_PREFILL_SCRATCH_MIB 64
+int kie_prefill_batched_noalloc(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
+
 /* Generates n_steps tokens in one launch.  out_tokens: device int32
  * [n_steps] (required when n_steps > 0).  out_logits: device fp32
  * [n_steps][vocab_out] or NULL.  n_steps == 0 is a no-op.

@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_create": (ctypes.c_int, [P(Config), P(Weights), VP, P(VP)]),
         "kie_prefill": (ctypes.c_int, [VP, P(I32), I32]),
         "kie_prefill_batched": (ctypes.c_int, [VP, P(I32), I32]),
+        "kie_prefill_batched_noalloc": (ctypes.c_int, [VP, P(I32), I32]),
         "kie_decode": (ctypes.c_int, [VP, I32, VP, VP]),
         "kie_decode_sampled": (ctypes.c_int, [VP, I32, ctypes.c_uint64, ctypes.c_float, VP, VP]),
         "kie_reset": (ctypes.c_int, [VP]),

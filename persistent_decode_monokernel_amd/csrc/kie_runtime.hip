@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -83,6 +84,7 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;
 namespace {
 constexpr int kPrefillChunk = 2048;                // positions per batched prefill chunk, at most
 size_t moe_max_tiles(size_t rows, int E);
+int scratch_setup(int dev);
 }  // namespace
 
 struct kie_handle {
@@ -444,6 +446,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
     h->moe_off.resize(c.n_experts + 1);
     h->moe_fill.resize(c.n_experts);
   }
+  if ((rc = scratch_setup(h->device))) return bail(rc);
   *out = h;
   g_err.clear();
   return KIE_OK;
@@ -725,6 +728,38 @@ int prefill_batched_run(kie_handle* h, const int32_t* tokens, int32_t n, int T, 
   return KIE_OK;
 }
 
+// ---- the no-allocation prefill's workspace: one static array per GPU
+constexpr size_t kScratchBytes = (size_t)KIE_PREFILL_SCRATCH_MIB << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device memory of the no-allocation prefill.  In host code this name is a
+// stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device (scratch_setup).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Looks up, once per device and with that device current, the device
+// address of `scratch`.
+int scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(KIE_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return KIE_OK;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(KIE_ERR_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+  g_scratch_ptr[dev] = ptr;
+  return KIE_OK;
+}
+
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 
 int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
@@ -747,6 +782,35 @@ int kie_prefill_batched(kie_handle* h, const int32_t* tokens, int32_t n) {
     h->pf_ws_bytes = need;
   }
   return prefill_batched_run(h, tokens, n, T, static_cast<char*>(h->pf_ws));
+}
+
+int kie_prefill_batched_noalloc(kie_handle* h, const int32_t* tokens, int32_t n) {
+  g_err.clear();
+  int rc = prefill_batched_check(h, tokens, n);
+  if (rc) return rc;
+  char* ws = static_cast<char*>(scratch_of(h->device));
+  if (!ws) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != h->device)
+      return fail(KIE_ERR_BAD_STATE, "the handle's device is not current");
+    if ((rc = scratch_setup(h->device))) return rc;
+    ws = static_cast<char*>(scratch_of(h->device));
+  }
+  // the largest chunk, up to the usual one, whose workspace fits the array
+  int T = std::max(1, std::min(kPrefillChunk, n - 1));
+  if (prefill_ws(h->base, 1, nullptr, nullptr) > kScratchBytes)
+    return fail(KIE_ERR_UNSUPPORTED, "one position's prefill workspace exceeds the " +
+                                         std::to_string(KIE_PREFILL_SCRATCH_MIB) +
+                                         " MiB static scratch; use kie_prefill_batched");
+  if (prefill_ws(h->base, T, nullptr, nullptr) > kScratchBytes) {
+    int lo = 1, hi = T;                       // lo fits, hi does not
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      (prefill_ws(h->base, mid, nullptr, nullptr) <= kScratchBytes ? lo : hi) = mid;
+    }
+    T = lo;
+  }
+  return prefill_batched_run(h, tokens, n, T, ws);
 }
 
 int kie_debug_gemm(const void* w, const float* a, float* c, int32_t m, int32_t n, int32_t k,

@@ -87,6 +87,13 @@ class Engine:
         check(self.lib.kie_prefill_batched(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                            int(t.size)), "kie_prefill_batched")
 
+    def prefill_batched_noalloc(self, tokens: Sequence[int]) -> None:
+        """kie_prefill_batched_noalloc: as prefill_batched, with the workspace in
+        the library's static device array (no device allocation)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        check(self.lib.kie_prefill_batched_noalloc(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                                   int(t.size)), "kie_prefill_batched_noalloc")
+
     def decode_into(self, n: int, out_tokens: Optional[torch.Tensor],
                     out_logits: Optional[torch.Tensor] = None) -> None:
         tp = out_tokens.data_ptr() if out_tokens is not None else None
