@@ -25,10 +25,29 @@ and this module defines it the way the decode kernel computes it:
   wins (the kernel folds packed float32 keys into the same argmax it uses for
   greedy decoding).
 
+Top-k and top-p (nucleus) sampling restrict that draw to a candidate set
+and are not defined on the pages either; the reading taken here:
+
+* Candidates are ordered by logit, largest first, ties by the lower index
+  (exactly the order of the greedy argmax).  Top-k keeps the first k of
+  them; with top-p and no top-k the pool is the first MAX_TOP_K (256), so a
+  nucleus wider than that is cut there.
+* Top-p then keeps the shortest prefix of the pool whose probability mass
+  reaches p times the pool's mass: q_j = exp((z_j - z_0) / T) in float64
+  (z_0 the largest logit), c = the running sum of q in pool order, and the
+  prefix ends at the first j with c_j >= p * c_last.
+* The token is the Gumbel-max draw (the keys above) over the kept set, the
+  first maximum (lowest index) winning.  Top-k 1 is therefore the greedy
+  token, and a pool of the whole vocabulary with p = 1 is plain temperature
+  sampling.
+
 Parity status: Philox is pinned against numpy's own Philox4x64-10 bit
 generator; the draw against the softmax distribution (chi-square over many
 counters), its zero-temperature limit (the greedy argmax) and its shift
-invariance.  See tests/test_oracle_sampling.py.
+invariance; top-k 1 against the greedy argmax, the whole-vocabulary pool
+against temperature sampling, the kept sets against brute force and the
+draws against the renormalised truncated softmax (chi-square).  See
+tests/test_oracle_sampling.py.
 """
 from __future__ import annotations
 
@@ -122,3 +141,46 @@ def sample_token(z: np.ndarray, temperature: float, seed: int, pos: int) -> int:
     """One draw from softmax(z / T): the first maximum of the keys."""
     keys = sample_keys(z, temperature, seed, pos)
     return int(np.argmax(keys))
+
+
+MAX_TOP_K = 256        # candidate pool of top-k / top-p sampling, at most
+
+
+def order_key(z: np.ndarray) -> np.ndarray:
+    """uint32 keys whose unsigned order is the float32 order of z (-0 below +0)."""
+    u = np.asarray(z, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    neg = (u & np.uint64(0x80000000)) != 0
+    return np.where(neg, np.uint64(0xFFFFFFFF) - u, u | np.uint64(0x80000000)).astype(np.uint64)
+
+
+def candidate_order(z: np.ndarray) -> np.ndarray:
+    """Vocabulary indices by logit, largest first, ties by the lower index."""
+    k = order_key(z)
+    idx = np.arange(k.shape[0])
+    return np.lexsort((idx, -k.astype(np.int64)))
+
+
+def kept_set(z: np.ndarray, temperature: float, top_k: int, top_p: float) -> np.ndarray:
+    """Indices (in candidate order) that top-k then top-p keep."""
+    V = int(np.asarray(z).shape[0])
+    K = min(top_k if top_k > 0 else MAX_TOP_K, V)
+    pool = candidate_order(z)[:K]
+    if top_p < 1.0:
+        z64 = np.asarray(z, dtype=np.float32).astype(np.float64)
+        t = float(np.float32(temperature))
+        q = np.exp((z64[pool] - z64[pool[0]]) / t)
+        c = np.cumsum(q)
+        m = int(np.argmax(c >= float(np.float32(top_p)) * c[-1])) + 1
+        pool = pool[:m]
+    return pool
+
+
+def sample_token_topkp(z: np.ndarray, temperature: float, seed: int, pos: int, top_k: int,
+                       top_p: float) -> int:
+    """One draw restricted by top-k (0: none) and top-p (1: none)."""
+    if top_k == 0 and top_p >= 1.0:
+        return sample_token(z, temperature, seed, pos)
+    keep = kept_set(z, temperature, top_k, top_p)
+    keys = sample_keys(z, temperature, seed, pos)[keep]
+    best = keys.max()
+    return int(keep[keys == best].min())

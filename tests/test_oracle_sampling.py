@@ -78,3 +78,96 @@ def test_keys_depend_on_seed_and_position_only_through_the_noise():
     assert np.array_equal(a, sample_keys(z, 1.0, seed=1, pos=0))
     assert not np.array_equal(a, sample_keys(z, 1.0, seed=2, pos=0))
     assert not np.array_equal(a, sample_keys(z, 1.0, seed=1, pos=1))
+
+
+# ---- top-k / top-p
+from oracle.sampling import MAX_TOP_K, candidate_order, kept_set, order_key, sample_token_topkp  # noqa: E402
+
+
+def test_candidate_order_is_value_descending_then_index_ascending():
+    z = np.array([1.0, 3.0, -2.0, 3.0, 0.0, -0.0, 1.0], dtype=np.float32)
+    # by hand: 3.0 at 1 and 3, then 1.0 at 0 and 6, then +0.0 (4) above -0.0 (5), then -2.0
+    assert list(candidate_order(z)) == [1, 3, 0, 6, 4, 5, 2]
+    # the key order is the float order on a brute-force sweep of ordinary values
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(2000).astype(np.float32)
+    k = order_key(v)
+    i, j = rng.integers(0, 2000, size=(2, 5000))
+    assert np.all((v[i] < v[j]) == (k[i] < k[j]))
+
+
+def test_top_k_one_is_the_greedy_token_including_ties():
+    rng = np.random.default_rng(1)
+    for pos in range(40):
+        z = np.round(rng.standard_normal(300), 1).astype(np.float32)   # many exact ties
+        assert sample_token_topkp(z, 1.3, seed=77, pos=pos, top_k=1, top_p=1.0) == argmax_first(z)
+    z = np.zeros(50, np.float32)
+    assert sample_token_topkp(z, 1.0, seed=5, pos=3, top_k=1, top_p=1.0) == 0
+
+
+def test_whole_vocabulary_pool_with_p_one_is_temperature_sampling():
+    rng = np.random.default_rng(2)
+    for pos in range(60):
+        z = rng.standard_normal(200).astype(np.float32)
+        want = sample_token(z, 0.9, seed=31, pos=pos)
+        assert sample_token_topkp(z, 0.9, seed=31, pos=pos, top_k=200, top_p=1.0) == want
+        assert sample_token_topkp(z, 0.9, seed=31, pos=pos, top_k=0, top_p=1.0) == want
+
+
+def test_kept_sets_match_brute_force():
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        z = np.round(rng.standard_normal(n) * 2, 1).astype(np.float32)
+        t = float(rng.choice([0.3, 1.0, 2.5]))
+        k = int(rng.integers(0, n + 3))
+        p = float(rng.choice([1.0, 0.9, 0.5, 0.05]))
+        keep = list(kept_set(z, t, k, p))
+        # brute force: sort pairs (-value, index), take k (all if 0), then the
+        # shortest prefix whose mass reaches p of the pool's mass
+        pairs = sorted(range(n), key=lambda i: (-float(z[i]), i))
+        pool = pairs[: min(k, n)] if k > 0 else pairs[: min(MAX_TOP_K, n)]
+        if p < 1.0:
+            q = [np.exp((float(z[i]) - float(z[pool[0]])) / float(np.float32(t))) for i in pool]
+            tot = float(np.cumsum(q)[-1])
+            run, m = 0.0, 0
+            for m, qi in enumerate(q, 1):
+                run += qi
+                if run >= float(np.float32(p)) * tot:
+                    break
+            pool = pool[:m]
+        assert keep == pool, (z, t, k, p, keep, pool)
+
+
+def _chi2(counts, probs, n):
+    expect = n * probs
+    return float(((counts - expect) ** 2 / expect).sum())
+
+
+def test_top_k_draws_follow_the_renormalised_softmax():
+    z = np.array([0.3, -1.2, 0.9, 0.0, 2.1, -0.4, 1.5, 0.7, -2.0, 0.1], dtype=np.float32)
+    t, k, n = 0.8, 4, 30000
+    draws = [sample_token_topkp(z, t, seed=99, pos=p, top_k=k, top_p=1.0) for p in range(n)]
+    counts = np.bincount(draws, minlength=z.size)
+    top = np.argsort(-z.astype(np.float64), kind="stable")[:k]
+    assert set(np.nonzero(counts)[0]) <= set(top.tolist())
+    q = np.exp(z[top].astype(np.float64) / np.float32(t))
+    # 3 degrees of freedom: P(chi2 > 21) ~ 1e-4
+    assert _chi2(counts[top], q / q.sum(), n) < 21.0
+
+
+def test_top_p_draws_follow_the_renormalised_nucleus():
+    z = np.array([2.0, 1.6, 1.0, 0.2, -0.5, -1.0, 0.9, 1.7], dtype=np.float32)
+    t, p, n = 1.0, 0.8, 30000
+    # nucleus by hand: probabilities sorted 2.0, 1.7, 1.6, 1.0, 0.9, 0.2, -0.5, -1.0
+    w = np.exp(np.array([2.0, 1.7, 1.6, 1.0, 0.9, 0.2, -0.5, -1.0]))
+    cum = np.cumsum(w) / w.sum()
+    m = int(np.argmax(cum >= np.float32(p))) + 1
+    assert m == 4                                                       # cum 0.29, 0.51, 0.71, 0.82
+    want = [0, 7, 1, 2]
+    assert list(kept_set(z, t, 0, p)) == want
+    draws = [sample_token_topkp(z, t, seed=4, pos=i, top_k=0, top_p=p) for i in range(n)]
+    counts = np.bincount(draws, minlength=z.size)
+    assert set(np.nonzero(counts)[0]) <= set(want)
+    q = np.exp(z[want].astype(np.float64))
+    assert _chi2(counts[want], q / q.sum(), n) < 25.0                  # m - 1 degrees of freedom
