@@ -216,6 +216,28 @@ int kie_decode(kie_handle *h, int32_t n_steps, int32_t *out_tokens, float *out_l
 int kie_decode_sampled(kie_handle *h, int32_t n_steps, uint64_t seed, float temperature,
                        int32_t *out_tokens, float *out_logits);
 
+/* As kie_decode_sampled with temperature > 0, with the draw restricted to
+ * top-k and top-p (nucleus) candidates; the pages name sampling in the
+ * monokernel but no rule (same passage as kie_decode_sampled).  Candidates
+ * are the vocabulary entries by logit, largest first, ties by the lower
+ * index.  top_k in [1, KIE_MAX_TOP_K] keeps the first top_k of them;
+ * top_k == 0 keeps the first KIE_MAX_TOP_K (so a nucleus wider than that is
+ * cut there).  top_p in (0, 1) then keeps the shortest prefix whose mass
+ * exp((z_j - z_0) / temperature), summed in float64 in that order (z_0 the
+ * largest logit), reaches top_p of the kept pool's mass; top_p == 1 keeps
+ * the pool.  The token is the Gumbel-max draw of kie_decode_sampled (same
+ * keys) over what is kept, the lowest index winning on equal keys; so
+ * top_k == 1 is the greedy token, and top_k == 0 with top_p == 1 is
+ * exactly kie_decode_sampled.  Every workgroup selects the candidates from
+ * the step's logits after the step's grid barrier.  KIE_ERR_INVALID_ARG for
+ * temperature <= 0, infinite or NaN, top_k outside [0, KIE_MAX_TOP_K] or
+ * top_p outside (0, 1]; KIE_ERR_UNSUPPORTED for a KIE_MODE_GRAPH handle
+ * (unless nothing restricts the draw).  Other arguments and errors as
+ * kie_decode. */
+#define KIE_MAX_TOP_K 256
+int kie_decode_sampled_topkp(kie_handle *h, int32_t n_steps, uint64_t seed, float temperature,
+                             int32_t top_k, float top_p, int32_t *out_tokens, float *out_logits);
+
 /* Drops the context: position 0, no pending token (KV contents are simply
  * overwritten by the next prefill).  Also clears a broken state. */
 int kie_reset(kie_handle *h);

@@ -1731,6 +1731,158 @@ __device__ __forceinline__ float sample_key(float v, float temperature, unsigned
   return (float)((double)v / (double)temperature + g);
 }
 
+// ---------------------------------------------------------------------------
+// Top-k / top-p draw (sample == 2).  Candidates are the logits in order,
+// largest first, ties by the lower index (the greedy argmax's order); top-k
+// keeps the first K of them (K = top_k, or kMaxTopK without one), top-p the
+// shortest prefix whose mass exp((z_j - z_0) / T), summed in float64 in
+// that order, reaches top_p of the kept pool's; the token is the Gumbel-max
+// draw of temperature sampling over what is kept, the lowest index winning
+// on equal keys.  Runs once the step's logits in p.zbuf are complete (after
+// the step's grid barrier); every workgroup computes the same token from
+// the same logits, so no exchange follows.  Called by every thread of the
+// workgroup; `lds`: kSelWords floats of scratch.
+// ---------------------------------------------------------------------------
+constexpr int kSelWords = 256 + kThreads + 8 + 4 * kMaxTopK;
+static_assert(kSelWords <= 2 * kPartCap, "selection scratch exceeds the GEMV scratch it reuses");
+
+__device__ __forceinline__ unsigned ord_key(float v) {
+  const unsigned u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(unsigned long long key) {
+  const unsigned u = (unsigned)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int key_index(unsigned long long key) {
+  return (int)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
+}
+
+__device__ int select_topkp(const Params& p, int step, float* lds) {
+  const int V = p.Vout, tid = threadIdx.x;
+  const int K = min(p.top_k > 0 ? p.top_k : kMaxTopK, V);
+  unsigned* hist = reinterpret_cast<unsigned*>(lds);               // [256]
+  unsigned* tcnt = hist + 256;                                      // [kThreads]
+  unsigned* misc = tcnt + kThreads;                                 // [8]
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(misc + 8);   // [kMaxTopK]
+  double* q = reinterpret_cast<double*>(cand + kMaxTopK);          // [kMaxTopK]
+  const float* zb = p.zbuf;
+  // 1. the K-th largest key, a byte at a time from the top: the count of
+  //    keys above the prefix's bucket decides the next byte
+  unsigned prefix = 0u, mask = 0u, r = (unsigned)K;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < V; i += kThreads) {
+      const unsigned u = ord_key(ld_c(zb + i));
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned above = 0u;
+      int d = 255;
+      for (; d > 0 && above + hist[d] < r; --d) above += hist[d];
+      misc[0] = (unsigned)d;
+      misc[1] = above;
+    }
+    __syncthreads();
+    prefix |= misc[0] << shift;
+    mask |= 0xFFu << shift;
+    r -= misc[1];
+    __syncthreads();
+  }
+  // 2. the keys above the K-th, and the first r equal to it in index order
+  //    (each thread takes a contiguous run of indices)
+  const int per = (V + kThreads - 1) / kThreads;
+  const int i0 = min(V, tid * per), i1 = min(V, i0 + per);
+  unsigned ties = 0u;
+  for (int i = i0; i < i1; ++i) ties += ord_key(ld_c(zb + i)) == prefix ? 1u : 0u;
+  tcnt[tid] = ties;
+  if (tid == 0) misc[2] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned acc = 0u;
+    for (int t = 0; t < kThreads; ++t) {
+      const unsigned v = tcnt[t];
+      tcnt[t] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  unsigned before = tcnt[tid];
+  for (int i = i0; i < i1; ++i) {
+    const unsigned u = ord_key(ld_c(zb + i));
+    const bool keep = u > prefix || (u == prefix && before < r);
+    before += u == prefix ? 1u : 0u;
+    if (keep) {
+      const unsigned slot = atomicAdd(&misc[2], 1u);     // exactly K keys are kept
+      if (slot < (unsigned)kMaxTopK) cand[slot] = ((unsigned long long)u << 32) | (0xFFFFFFFFu - (unsigned)i);
+    }
+  }
+  __syncthreads();
+  // 3. the K candidates in candidate order (their packed keys, descending):
+  //    a bitonic sort, padded with zero keys that sort last
+  int n2 = 1;
+  while (n2 < K) n2 <<= 1;
+  for (int j = K + tid; j < n2; j += kThreads) cand[j] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int j = tid; j < n2; j += kThreads) {
+        const int o = j ^ stride;
+        if (o > j) {
+          const unsigned long long a = cand[j], b = cand[o];
+          if ((j & size) == 0 ? a < b : a > b) {
+            cand[j] = b;
+            cand[o] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  // 4. top-p: the shortest prefix reaching top_p of the pool's mass
+  int m = K;
+  if (p.top_p < 1.0f) {
+    const double z0 = (double)key_value(cand[0]), t = (double)p.temperature;
+    for (int j = tid; j < K; j += kThreads) q[j] = exp(((double)key_value(cand[j]) - z0) / t);
+    __syncthreads();
+    if (tid == 0) {
+      double tot = 0.0;
+      for (int j = 0; j < K; ++j) tot += q[j];
+      const double goal = (double)p.top_p * tot;
+      double run = 0.0;
+      int j = 0;
+      for (; j < K - 1; ++j) {
+        run += q[j];
+        if (run >= goal) break;
+      }
+      misc[3] = (unsigned)(j + 1);
+    }
+    __syncthreads();
+    m = (int)misc[3];
+  }
+  // 5. Gumbel-max over the kept candidates
+  const int pos = p.pos0 + step;
+  unsigned long long best = 0ull;
+  for (int j = tid; j < m; j += kThreads) {
+    const int idx = key_index(cand[j]);
+    const unsigned long long k = argmax_key(sample_key(key_value(cand[j]), p.temperature, p.seed, pos, idx), idx);
+    best = k > best ? k : best;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(best, o, 64);
+    best = other > best ? other : best;
+  }
+  unsigned long long* red = reinterpret_cast<unsigned long long*>(tcnt);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = best;
+  __syncthreads();
+  unsigned long long b = 0ull;
+  for (int w = 0; w < kWaves; ++w) b = red[w] > b ? red[w] : b;
+  __syncthreads();                                   // the scratch is free again
+  return argmax_index(b, V);
+}
+
 __device__ __forceinline__ GemvWork lm_work(const Params& p, int wg) {
   return gemv_work(p.Vout, p.d, p.n_wg, wg, 1);
 }
@@ -1753,7 +1905,8 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
   const float inv = rmsnorm_lds(p, p.final_norm, G, s.h, s.red);
   mark(tr);
   float* logits = p.out_logits ? p.out_logits + (size_t)step * p.Vout : nullptr;
-  const bool sample = p.sample != 0;
+  const bool sample = p.sample == 1;
+  const bool select = p.sample == 2;       // the logits go to zbuf; the draw follows the barrier
   const int pos = p.pos0 + step;           // position of this step's input token
   unsigned long long best = 0ull;
   gemv_run<true>(g, addr, s.h, s.part, s.sums, pre,
@@ -1761,6 +1914,10 @@ __device__ __forceinline__ bool stage_lmhead(const Params& p, int step, int wg, 
                    for (int i = threadIdx.x; i < n; i += kThreads) {
                      const float v = sums[i] * inv;
                      if (logits) logits[b0 + i] = v;
+                     if (select) {
+                       st_c(p.zbuf + b0 + i, v);
+                       continue;
+                     }
                      const float key = sample ? sample_key(v, p.temperature, p.seed, pos, b0 + i) : v;
                      const unsigned long long k = argmax_key(key, b0 + i);
                      best = k > best ? k : best;
@@ -1835,7 +1992,7 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   auto resolve = [&](int prev) -> int {
     const Params& p = fresh(pp);
     if (!decode) return p.prompt[prev + 1];
-    const int t = argmax_index(ld_c64(p.amax + (prev & 1)), p.Vout);
+    const int t = p.sample == 2 ? select_topkp(p, prev, s.part) : argmax_index(ld_c64(p.amax + (prev & 1)), p.Vout);
     if (wg == 0 && threadIdx.x == 0) {
       p.out_tokens[prev] = t;
       st_c64(p.amax + ((prev + 1) & 1), 0ull);

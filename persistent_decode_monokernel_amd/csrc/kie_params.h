@@ -15,6 +15,7 @@ constexpr int kMaxHeadDim = 128;           // 16 lanes x 8 fp16 per K/V row
 constexpr int kMaxActiveExperts = 16;      // top_k + shared
 constexpr int kBatch = 4;                  // GEMV: 16-byte loads per lane per batch
 constexpr int kPartCap = 2048;             // GEMV: per-block task partials in LDS (floats)
+constexpr int kMaxTopK = 256;              // top-k / top-p candidate pool, at most
 constexpr int kGroups = 8;                 // grid barrier: arrival groups (one per XCD)
 constexpr int kGroupStride = 64;           // grid barrier: words between counters (256 B)
 constexpr int kBarrierWords = kGroupStride * (1 + kGroups);
@@ -78,9 +79,13 @@ struct Params {
   unsigned long long* trace;    // [n_wg][kTraceEvents] barrier clock stamps, or nullptr
   int trace_step;               // the decode step that is traced
   // ---- per call: how a decode step picks its token
-  int sample;                   // 0: greedy argmax; 1: temperature sampling (Gumbel-max)
+  int sample;                   // 0: greedy argmax; 1: temperature sampling (Gumbel-max);
+                                // 2: the same draw restricted by top-k / top-p
   float temperature;            // > 0 when sampling
   unsigned long long seed;      // sampling key (Philox4x64 key word 0)
+  int top_k;                    // sample == 2: candidates kept, 1..kMaxTopK (0: the whole pool)
+  float top_p;                  // sample == 2: nucleus mass, (0, 1]
+  float* zbuf;                  // [Vout] the step's logits, for the top-k / top-p selection
 };
 
 // Host-visible launchers implemented next to the kernels.

@@ -393,6 +393,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   KIE_ALLOC(amax, unsigned long long, 2);
   KIE_ALLOC(err, int, 1);
   KIE_ALLOC(state, int, 4);
+  KIE_ALLOC(zbuf, float, c.vocab_out);
   KIE_ALLOC(expert_log, int, c.n_experts ? cap * c.n_layers * c.top_k : 1);
   if (c.flags & KIE_TRACE) {
     KIE_ALLOC(trace, unsigned long long, (size_t)p.n_wg * kie::kTraceEvents);
@@ -477,8 +478,8 @@ int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
 }
 
 namespace {
-int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, bool sample,
-                 float temperature, uint64_t seed);
+int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
+                 float temperature, uint64_t seed, int top_k = 0, float top_p = 1.f);
 
 // Batched prefill of positions 0 .. n - 2 in chunks of kPrefillChunk positions.
 // Per chunk and layer: RMSNorm -> Q/K/V products -> RoPE + fp16 K/V rows into
@@ -841,7 +842,7 @@ int kie_debug_gemm(const void* w, const float* a, float* c, int32_t m, int32_t n
 
 int kie_decode(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits) {
   g_err.clear();
-  return decode_steps(h, n, out_tokens, out_logits, false, 0.f, 0ull);
+  return decode_steps(h, n, out_tokens, out_logits, 0, 0.f, 0ull);
 }
 
 int kie_decode_sampled(kie_handle* h, int32_t n, uint64_t seed, float temperature, int32_t* out_tokens,
@@ -849,12 +850,27 @@ int kie_decode_sampled(kie_handle* h, int32_t n, uint64_t seed, float temperatur
   g_err.clear();
   if (!(temperature >= 0.f) || !std::isfinite(temperature))
     return fail(KIE_ERR_INVALID_ARG, "temperature must be finite and >= 0");
-  return decode_steps(h, n, out_tokens, out_logits, temperature > 0.f, temperature, seed);
+  return decode_steps(h, n, out_tokens, out_logits, temperature > 0.f ? 1 : 0, temperature, seed);
+}
+
+int kie_decode_sampled_topkp(kie_handle* h, int32_t n, uint64_t seed, float temperature, int32_t top_k,
+                             float top_p, int32_t* out_tokens, float* out_logits) {
+  g_err.clear();
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(KIE_ERR_INVALID_ARG, "temperature must be finite and > 0");
+  if (top_k < 0 || top_k > kie::kMaxTopK)
+    return fail(KIE_ERR_INVALID_ARG, "top_k must be in [0, " + std::to_string(kie::kMaxTopK) + "]");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(KIE_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  if (top_k == 0 && top_p == 1.f)      // nothing restricts the draw: plain temperature sampling
+    return decode_steps(h, n, out_tokens, out_logits, 1, temperature, seed);
+  if (h && (h->cfg.flags & KIE_MODE_GRAPH))
+    return fail(KIE_ERR_UNSUPPORTED, "top-k / top-p sampling runs in the persistent mode only");
+  return decode_steps(h, n, out_tokens, out_logits, 2, temperature, seed, top_k, top_p);
 }
 
 namespace {
-int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, bool sample,
-                 float temperature, uint64_t seed) {
+int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
+                 float temperature, uint64_t seed, int top_k, float top_p) {
   if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
   if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
   if (n < 0) return fail(KIE_ERR_INVALID_ARG, "n_steps < 0");
@@ -874,9 +890,11 @@ int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logit
   p.out_tokens = out_tokens;
   p.out_logits = out_logits;
   p.trace_step = n > 1 ? 1 : 0;
-  p.sample = sample ? 1 : 0;
+  p.sample = sample;
   p.temperature = sample ? temperature : 0.f;
   p.seed = sample ? (unsigned long long)seed : 0ull;
+  p.top_k = sample == 2 ? top_k : 0;
+  p.top_p = sample == 2 ? top_p : 1.f;
   rc = run_steps(h, p);
   if (rc) return rc;
   h->pos += n;

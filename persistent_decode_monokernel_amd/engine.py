@@ -108,13 +108,26 @@ class Engine:
         check(self.lib.kie_decode_sampled(self.h, int(n), ctypes.c_uint64(int(seed) & (2**64 - 1)),
                                           ctypes.c_float(float(temperature)), tp, lp), "kie_decode_sampled")
 
-    def decode(self, n: int, logits: bool = True, seed: Optional[int] = None, temperature: float = 0.0):
-        """n decode steps; greedy unless a seed and a temperature > 0 are given."""
+    def decode_topkp_into(self, n: int, seed: int, temperature: float, top_k: int, top_p: float,
+                          out_tokens: Optional[torch.Tensor], out_logits: Optional[torch.Tensor] = None) -> None:
+        """kie_decode_sampled_topkp: the temperature draw restricted by top-k / top-p."""
+        tp = out_tokens.data_ptr() if out_tokens is not None else None
+        lp = out_logits.data_ptr() if out_logits is not None else None
+        check(self.lib.kie_decode_sampled_topkp(self.h, int(n), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                                ctypes.c_float(float(temperature)), int(top_k),
+                                                ctypes.c_float(float(top_p)), tp, lp), "kie_decode_sampled_topkp")
+
+    def decode(self, n: int, logits: bool = True, seed: Optional[int] = None, temperature: float = 0.0,
+               top_k: Optional[int] = None, top_p: Optional[float] = None):
+        """n decode steps; greedy unless a seed and a temperature > 0 are given
+        (then restricted by top_k / top_p when either is given)."""
         dev = self._weights["tok_emb"].device
         toks = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
         lg = torch.empty((max(n, 1), self.model.vocab_out), dtype=torch.float32, device=dev) if logits else None
         if seed is None:
             self.decode_into(n, toks, lg)
+        elif top_k is not None or top_p is not None:
+            self.decode_topkp_into(n, seed, temperature, top_k or 0, 1.0 if top_p is None else top_p, toks, lg)
         else:
             self.decode_sampled_into(n, seed, temperature, toks, lg)
         return toks[:n], (lg[:n] if lg is not None else None)

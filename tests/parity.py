@@ -186,3 +186,40 @@ def compare_sampled_steps(z_gpu: np.ndarray, tok_gpu: np.ndarray, z_or: np.ndarr
             cross += 1
             assert int(tok_gpu[i]) == int(oo[0]), f"step {i}: gpu token differs from the oracle's own draw"
     return {"steps": n, "pinned": pinned, "unpinned": unpinned, "cross_checked": cross, "worst_abs": worst}
+
+
+CUT_MARGIN = 1e-12     # relative float64 slack at a top-p cut (exp and rounding order)
+
+
+def check_topkp_step(z_gpu: np.ndarray, tok: int, temperature: float, seed: int, pos: int, top_k: int,
+                     top_p: float) -> bool:
+    """The kernel's top-k / top-p draw against the oracle's, recomputed from
+    the kernel's own logits.  Returns True if the step is pinned (the
+    oracle's draw is unambiguous and the token equals it); otherwise the
+    token must still be a draw the oracle could make within float64 slack:
+    one of the two best keys over a kept set that differs from the oracle's
+    by at most the candidate at the cut."""
+    from oracle.sampling import MAX_TOP_K, candidate_order, kept_set, sample_keys, sample_token_topkp
+    keep = kept_set(z_gpu, temperature, top_k, top_p)
+    keys = sample_keys(z_gpu, temperature, seed, pos).astype(np.float64)
+    kk = np.sort(keys[keep])[::-1]
+    cut_close = False
+    if top_p < 1.0:
+        pool = candidate_order(z_gpu)[: min(top_k if top_k > 0 else MAX_TOP_K, z_gpu.shape[0])]
+        z64 = np.asarray(z_gpu, np.float32).astype(np.float64)
+        q = np.exp((z64[pool] - z64[pool[0]]) / float(np.float32(temperature)))
+        c = np.cumsum(q)
+        goal = float(np.float32(top_p)) * c[-1]
+        m = len(keep)
+        near = [abs(c[m - 1] - goal)] + ([abs(c[m - 2] - goal)] if m >= 2 else [])
+        cut_close = min(near) <= CUT_MARGIN * goal
+    key_close = len(kk) > 1 and kk[0] - kk[1] <= KEY_MARGIN * max(1.0, abs(kk[0]))
+    if not cut_close and not key_close:
+        assert tok == sample_token_topkp(z_gpu, temperature, seed, pos, top_k, top_p), (tok, pos)
+        return True
+    # the kept set may gain the candidate at the cut; the draw may be either
+    # of the two best keys over it
+    cand = list(kept_set(z_gpu, temperature, top_k, 1.0))[: len(keep) + 1] if cut_close else list(keep)
+    order = sorted((int(i) for i in cand), key=lambda i: (-keys[i], i))
+    assert tok in order[:2], (tok, pos, order[:2])
+    return False

@@ -131,3 +131,75 @@ def test_2b_full_vocab_sampled_draws(torch, kie):
         else:
             assert int(toks[i]) in (int(order[0]), int(order[1])), i
     eng.close()
+
+
+# ---- top-k / top-p
+from tests.parity import ABS_TOL, check_topkp_step  # noqa: E402
+
+
+@pytest.mark.parametrize("name,temperature,top_k,top_p", [
+    ("tiny", 1.0, 1, 1.0), ("tiny", 0.8, 5, 1.0), ("tiny", 1.2, 0, 0.9), ("tiny", 0.7, 40, 0.6),
+    ("tiny", 2.0, 256, 0.97), ("2b", 1.0, 50, 0.9), ("2b", 0.6, 0, 0.95)])
+def test_topkp_draws_match_the_oracle_sampler(torch, kie, name, temperature, top_k, top_p):
+    """Each token is recomputed by the oracle's top-k / top-p sampler from the
+    kernel's own logits (pinned unless a key or the nucleus cut is within
+    float64 slack); the logits follow a teacher-forced oracle replay."""
+    cfg = get_config(name, n_layers=2) if name == "2b" else get_config(name)
+    _say("top-k/top-p", name, temperature, top_k, top_p)
+    W = make_weights(cfg, seed=0, device="cuda")
+    prompt = make_prompt(cfg)
+    P = len(prompt)
+    n = 16
+    seed = 0xC0FFEE + top_k
+    eng = kie.Engine(cfg, W, max_seq=P + n + 4)
+    eng.prefill(prompt)
+    toks, z = eng.decode(n, seed=seed, temperature=temperature, top_k=top_k, top_p=top_p)
+    toks, z = toks.cpu().numpy(), z.cpu().numpy()
+    assert eng.position == P - 1 + n
+    pinned = sum(check_topkp_step(z[i], int(toks[i]), temperature, seed, P - 1 + i, top_k, top_p)
+                 for i in range(n))
+    assert pinned >= n - 2, pinned
+    if top_k == 1:
+        np.testing.assert_array_equal(toks, np.argmax(z, axis=1))     # the greedy token
+    o = Oracle(cfg, weights_to_numpy(W))
+    o.prefill(prompt)
+    _, zo = o.decode(n, force=toks)
+    assert float(np.max(np.abs(z.astype(np.float64) - zo))) <= ABS_TOL
+    eng.close()
+
+
+def test_topkp_is_deterministic_composable_and_validated(torch, kie):
+    cfg = get_config("tiny")
+    _say("top-k/top-p determinism")
+    W = make_weights(cfg, seed=0, device="cuda")
+    prompt = make_prompt(cfg)
+    eng = kie.Engine(cfg, W)
+    eng.prefill(prompt)
+    t1, z1 = eng.decode(20, seed=7, temperature=1.0, top_k=30, top_p=0.8)
+    eng.reset()
+    eng.prefill(prompt)
+    ta, _ = eng.decode(8, seed=7, temperature=1.0, top_k=30, top_p=0.8)
+    tb, _ = eng.decode(12, seed=7, temperature=1.0, top_k=30, top_p=0.8)
+    np.testing.assert_array_equal(np.concatenate([ta.cpu().numpy(), tb.cpu().numpy()]), t1.cpu().numpy())
+    # no restriction is plain temperature sampling, bit for bit
+    eng.reset()
+    eng.prefill(prompt)
+    tu, zu = eng.decode(20, seed=7, temperature=1.0, top_k=0, top_p=1.0)
+    eng.reset()
+    eng.prefill(prompt)
+    ts, zs = eng.decode(20, seed=7, temperature=1.0)
+    np.testing.assert_array_equal(tu.cpu().numpy(), ts.cpu().numpy())
+    pos = eng.position
+    out = torch.empty(4, dtype=torch.int32, device="cuda")
+    for t, k, p in ((0.0, 5, 0.9), (1.0, -1, 0.9), (1.0, 257, 0.9), (1.0, 5, 0.0), (1.0, 5, 1.5),
+                    (float("nan"), 5, 0.9), (1.0, 5, float("nan"))):
+        with pytest.raises(RuntimeError):
+            eng.decode_topkp_into(4, 1, t, k, p, out)
+        assert eng.position == pos
+    eng.close()
+    # the staged mode refuses a restricted draw, before any launch
+    g = kie.Engine(cfg, W, graph=True)
+    g.prefill(prompt)
+    with pytest.raises(RuntimeError):
+        g.decode_topkp_into(4, 1, 1.0, 5, 0.9, out)
+    g.close()
