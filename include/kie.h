@@ -132,7 +132,10 @@ typedef struct kie_weights {
 typedef struct kie_handle kie_handle;
 
 /* Validates a configuration on the host only (no GPU needed).
- * KIE_OK, KIE_ERR_INVALID_ARG or KIE_ERR_UNSUPPORTED. */
+ * KIE_OK, KIE_ERR_INVALID_ARG or KIE_ERR_UNSUPPORTED.  The pages describe
+ * no API; the shapes are those of the model they benchmark, a 2B-class
+ * decoder (page "Breaking the memory wall: 3,000 tokens/s inference on
+ * standard GPUs", introduction). */
 int kie_config_check(const kie_config *cfg);
 
 /* Creates a decoder on the current HIP device.  Validates cfg and that every
@@ -141,7 +144,9 @@ int kie_config_check(const kie_config *cfg);
  * scratch, barrier words and the RoPE cos/sin table (built in float64,
  * rounded to fp32).  `hip_stream` (a hipStream_t, NULL = default stream) is
  * the stream every later launch of this handle uses.  On success *out owns
- * all of that memory until kie_destroy. */
+ * all of that memory until kie_destroy.  KIE_ERR_OCCUPANCY if the
+ * persistent grid cannot be co-resident: the monokernel stays resident for
+ * the whole decode (same page, section "1. The Monokernel Runtime"). */
 int kie_create(const kie_config *cfg, const kie_weights *w, void *hip_stream,
                kie_handle **out);
 
@@ -149,7 +154,10 @@ int kie_create(const kie_config *cfg, const kie_weights *w, void *hip_stream,
  * runs positions 0..n_tokens-2 through every layer (no lm_head) in one
  * persistent launch; tokens[n_tokens-1] becomes pending.  Needs a fresh or
  * reset handle (else KIE_ERR_BAD_STATE); KIE_ERR_TOKEN_RANGE for an id
- * outside [0, vocab_in); KIE_ERR_CONTEXT_OVERFLOW if n_tokens > max_seq. */
+ * outside [0, vocab_in); KIE_ERR_CONTEXT_OVERFLOW if n_tokens > max_seq.
+ * The prompt runs in the same GPU-resident program as decoding, without
+ * returning to the host between positions (same page, section "1. The
+ * Monokernel Runtime"). */
 int kie_prefill(kie_handle *h, const int32_t *tokens, int32_t n_tokens);
 
 /* As kie_prefill (same arguments, state afterwards and errors), but the
@@ -196,7 +204,12 @@ int kie_prefill_batched_noalloc(kie_handle *h, const int32_t *tokens, int32_t n_
 /* Generates n_steps tokens in one launch.  out_tokens: device int32
  * [n_steps] (required when n_steps > 0).  out_logits: device fp32
  * [n_steps][vocab_out] or NULL.  n_steps == 0 is a no-op.
- * KIE_ERR_CONTEXT_OVERFLOW if position + n_steps > max_seq. */
+ * KIE_ERR_CONTEXT_OVERFLOW if position + n_steps > max_seq.  One kernel
+ * launch for all the steps, with the greedy token fed back on the device:
+ * the single-request decode the pages measure (same page, introduction
+ * and section "1. The Monokernel Runtime"; launch overhead and CPU
+ * sampling are among the losses listed in "Where the microseconds are
+ * lost"). */
 int kie_decode(kie_handle *h, int32_t n_steps, int32_t *out_tokens, float *out_logits);
 
 /* As kie_decode, but each step draws its token from softmax(z / temperature)
@@ -262,6 +275,51 @@ int kie_last_elapsed_ms(const kie_handle *h, float *ms);
  * K rows are stored after RoPE. */
 int kie_debug_read_kv(const kie_handle *h, int32_t layer, int32_t pos0, int32_t pos1,
                       void *k_host, void *v_host);
+
+/* Test-only: one decode stage at a time, for checking each stage against a
+ * float64 computation (the pages describe the stages only as the parts of
+ * the monokernel: page "Breaking the memory wall: 3,000 tokens/s inference
+ * on standard GPUs", section "1. The Monokernel Runtime").  On a handle with
+ * a pending token (after a prefill), kie_debug_stage runs `stage` of layer
+ * `layer` (0 for KIE_STAGE_LM_HEAD) of the next decode step, at the
+ * handle's position, as the staged mode's kernels do (the attention stage
+ * includes its split merge).  KIE_STAGE_QKV at layer 0 opens the step;
+ * later stages read what the earlier ones of that step wrote, so they run
+ * in model order.  The attention stage writes its K/V rows into the cache
+ * (kie_debug_read_kv sees them); the position does not advance and the
+ * next prefill, decode or reset closes the step.  KIE_ERR_BAD_STATE
+ * without a pending token or an open step; KIE_ERR_INVALID_ARG for a stage
+ * the model lacks or a layer out of range. */
+#define KIE_STAGE_QKV 0          /* RMSNorm + Q/K/V products          */
+#define KIE_STAGE_ATTENTION 1    /* RoPE, K/V append, split attention, merge */
+#define KIE_STAGE_O 2            /* O product + residual              */
+#define KIE_STAGE_GATEUP 3       /* RMSNorm + gate/up products + SwiGLU */
+#define KIE_STAGE_DOWN 4         /* down product + residual           */
+#define KIE_STAGE_ROUTER 5       /* MoE: RMSNorm + router product     */
+#define KIE_STAGE_MOE_GATEUP 6   /* MoE: routing + experts' gate/up + SwiGLU */
+#define KIE_STAGE_MOE_DOWN 7     /* MoE: experts' down + residual     */
+#define KIE_STAGE_LM_HEAD 8      /* final RMSNorm + lm_head + argmax  */
+int kie_debug_stage(kie_handle *h, int32_t stage, int32_t layer);
+
+/* Test-only: copies what a stage of the open step (kie_debug_stage) wrote
+ * to `out_host`, at least n elements, as fp32 (int32 for KIE_ACT_TOKEN):
+ * the residual stream after the O product or after the FFN of `layer`
+ * ([d_model]), its q|k|v ([n_heads + 2 n_kv_heads][head_dim]), the
+ * attention output o ([n_heads][head_dim]), the FFN hidden u ([ffn_hidden],
+ * MoE: [top_k + shared][expert_hidden]), the router logits ([n_experts]),
+ * the logits ([vocab_out]) or the argmax token.  o and u cross between
+ * workgroups as 24-bit values (a 16-bit significand) and are returned so.
+ * KIE_ERR_BAD_STATE if a word was not written by that stage of the open
+ * step (checked by its epoch). */
+#define KIE_ACT_X_ATTN 0
+#define KIE_ACT_X 1
+#define KIE_ACT_QKV 2
+#define KIE_ACT_O 3
+#define KIE_ACT_U 4
+#define KIE_ACT_ROUTER 5
+#define KIE_ACT_LOGITS 6
+#define KIE_ACT_TOKEN 7
+int kie_debug_read_act(const kie_handle *h, int32_t what, int32_t layer, void *out_host, int32_t n);
 
 /* MoE only: the routed expert ids chosen at positions [pos0, pos1) by
  * prefill or decode, host int32 [pos1-pos0][n_layers][top_k] in rank order

@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_prefill_batched_noalloc": (ctypes.c_int, [VP, P(I32), I32]),
         "kie_decode": (ctypes.c_int, [VP, I32, VP, VP]),
         "kie_decode_sampled": (ctypes.c_int, [VP, I32, ctypes.c_uint64, ctypes.c_float, VP, VP]),
+        "kie_debug_stage": (ctypes.c_int, [VP, I32, I32]),
+        "kie_debug_read_act": (ctypes.c_int, [VP, I32, I32, VP, I32]),
         "kie_decode_sampled_topkp": (ctypes.c_int, [VP, I32, ctypes.c_uint64, ctypes.c_float, I32,
                                                     ctypes.c_float, VP, VP]),
         "kie_reset": (ctypes.c_int, [VP]),

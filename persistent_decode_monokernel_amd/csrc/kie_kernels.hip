@@ -2234,6 +2234,15 @@ hipError_t launch_staged_step(const Params& p, size_t lds_bytes, hipStream_t s) 
   return hipGetLastError();
 }
 
+// One stage of the staged mode (the attention stage with its merge).
+hipError_t launch_stage(const Params& p, size_t lds_bytes, int stage, int l, hipStream_t s) {
+  const dim3 grid(p.n_wg), block(kThreads);
+  const unsigned lds = (unsigned)lds_bytes;
+  hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, stage, l);
+  if (stage == kSAttn && p.splits > 1) hipLaunchKernelGGL(stage_kernel, grid, block, lds, s, p, (int)kSMerge, l);
+  return hipGetLastError();
+}
+
 size_t gemv_lds_bytes(int cols) {
   return ((size_t)((cols + 63) & ~63) + 2 * kPartCap) * sizeof(float);
 }

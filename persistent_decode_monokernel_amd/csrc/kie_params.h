@@ -94,6 +94,9 @@ int max_blocks_per_cu(int group, size_t lds_bytes);
 hipError_t launch_mono(const Params& p, const Params* p_dev, size_t lds_bytes, bool plain,
                        hipStream_t s);
 hipError_t launch_staged_step(const Params& p, size_t lds_bytes, hipStream_t s);
+// stage: the staged mode's stage numbering (kSQkv = 0, kSAttn, kSMerge, kSO, kSGateUp, kSDown,
+// kSRouter, kSMoeGateUp, kSMoeDown, kSLm); kSAttn also runs the merge
+hipError_t launch_stage(const Params& p, size_t lds_bytes, int stage, int l, hipStream_t s);
 hipError_t launch_gemv(const __half* w, const float* x, float* y, int rows, int cols, int n_wg,
                        hipStream_t s);
 size_t gemv_lds_bytes(int cols);

@@ -108,6 +108,7 @@ struct kie_handle {
   int last_decode_steps = 0;
   int trace_events = 0;          // events per workgroup recorded by the last decode
   unsigned epoch_next = 1;       // first activation epoch of the next launch
+  unsigned dbg_epoch0 = 0;       // kie_debug_stage: epochs of the open stage-by-stage step (0: none)
   void* pf_ws = nullptr;         // batched prefill workspace (grown on demand, freed with the handle)
   size_t pf_ws_bytes = 0;
   // MoE batched prefill: host copies of one chunk's routing and grouping,
@@ -180,6 +181,7 @@ int assign_epochs(kie_handle* h, kie::Params& p) {
 
 // Runs p.n_steps steps (prefill or decode) in the handle's mode.
 int run_steps(kie_handle* h, kie::Params& p) {
+  h->dbg_epoch0 = 0;
   int rc = reset_sync_words(h);
   if (rc) return rc;
   if ((rc = assign_epochs(h, p))) return rc;
@@ -919,6 +921,7 @@ int kie_reset(kie_handle* h) {
   h->pending = false;
   h->broken = false;
   h->last_decode_steps = 0;
+  h->dbg_epoch0 = 0;
   return KIE_OK;
 }
 
@@ -1103,6 +1106,122 @@ int kie_debug_stream(const void* src, void* dst, size_t bytes, int32_t n_wg, int
   if (e1) (void)hipEventDestroy(e1);
   (void)hipFree(sink);
   return rc;
+}
+
+// ---- one decode stage at a time (test-only)
+namespace {
+// kie.h's KIE_STAGE_* in the staged mode's stage numbering
+constexpr int kStageMap[] = {0, 1, 3, 4, 5, 6, 7, 8, 9};
+constexpr int kNumStages = (int)(sizeof(kStageMap) / sizeof(kStageMap[0]));
+constexpr int kSlotQkv = 0, kSlotO = 2, kSlotXO = 3, kSlotRouter = 4, kSlotU = 5, kSlotXDown = 6;
+
+kie::Params debug_params(const kie_handle* h) {
+  kie::Params p = h->base;
+  p.trace = nullptr;
+  p.mode = kie::kDecode;
+  p.n_steps = 1;
+  p.pos0 = h->pos;
+  p.epoch0 = h->dbg_epoch0;
+  p.out_tokens = nullptr;
+  p.out_logits = h->base.zbuf;      // the LM-head stage's logits, for kie_debug_read_act
+  p.sample = 0;
+  return p;
+}
+}  // namespace
+
+int kie_debug_stage(kie_handle* h, int32_t stage, int32_t layer) {
+  g_err.clear();
+  if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
+  if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
+  if (!h->pending) return fail(KIE_ERR_BAD_STATE, "no pending token: call kie_prefill first");
+  if (stage < 0 || stage >= kNumStages) return fail(KIE_ERR_INVALID_ARG, "unknown stage");
+  const bool moe = h->cfg.n_experts != 0;
+  const bool ffn_stage = stage == KIE_STAGE_GATEUP || stage == KIE_STAGE_DOWN;
+  const bool moe_stage = stage == KIE_STAGE_ROUTER || stage == KIE_STAGE_MOE_GATEUP || stage == KIE_STAGE_MOE_DOWN;
+  if ((moe && ffn_stage) || (!moe && moe_stage))
+    return fail(KIE_ERR_INVALID_ARG, moe ? "a MoE model has no dense FFN stage" : "a dense model has no MoE stage");
+  if (stage == KIE_STAGE_LM_HEAD ? layer != 0 : (layer < 0 || layer >= h->cfg.n_layers))
+    return fail(KIE_ERR_INVALID_ARG, "layer out of range (0 for the LM head)");
+  if ((long long)h->pos + 1 > h->cfg.max_seq) return fail(KIE_ERR_CONTEXT_OVERFLOW, "no room for a decode step");
+  if (stage == KIE_STAGE_QKV && layer == 0) {
+    // opens a step: fresh epochs, cleared argmax slot, step counter 0
+    kie::Params p = debug_params(h);
+    int rc = reset_sync_words(h);
+    if (rc) return rc;
+    if ((rc = assign_epochs(h, p))) return rc;
+    h->dbg_epoch0 = p.epoch0;
+  } else if (h->dbg_epoch0 == 0) {
+    return fail(KIE_ERR_BAD_STATE, "open a step with KIE_STAGE_QKV at layer 0 first");
+  }
+  const kie::Params p = debug_params(h);
+  KIE_HIP(kie::launch_stage(p, h->lds, kStageMap[stage], layer, h->stream));
+  KIE_HIP(hipStreamSynchronize(h->stream));
+  int err = 0;
+  KIE_HIP(hipMemcpy(&err, h->base.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err != 0) {
+    h->broken = true;
+    return fail(KIE_ERR_HIP, "device reported error " + std::to_string(err));
+  }
+  return KIE_OK;
+}
+
+int kie_debug_read_act(const kie_handle* h, int32_t what, int32_t layer, void* out_host, int32_t n) {
+  g_err.clear();
+  if (!h || !out_host) return fail(KIE_ERR_INVALID_ARG, "handle or out is NULL");
+  if (h->dbg_epoch0 == 0) return fail(KIE_ERR_BAD_STATE, "no step open (kie_debug_stage)");
+  const kie::Params& b = h->base;
+  const kie_config& c = h->cfg;
+  const int qd = c.n_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  const int ucount = c.n_experts ? (c.top_k + c.n_shared_experts) * c.expert_hidden : c.ffn_hidden;
+  if (layer < 0 || layer >= c.n_layers) return fail(KIE_ERR_INVALID_ARG, "layer out of range");
+  auto flag = [&](int slot) { return h->dbg_epoch0 + (unsigned)layer * 8u + (unsigned)slot; };
+  if (what == KIE_ACT_LOGITS || what == KIE_ACT_TOKEN) {
+    const int need = what == KIE_ACT_LOGITS ? c.vocab_out : 1;
+    if (n < need) return fail(KIE_ERR_INVALID_ARG, "out too small");
+    if (what == KIE_ACT_LOGITS) {
+      KIE_HIP(hipMemcpy(out_host, b.zbuf, sizeof(float) * c.vocab_out, hipMemcpyDeviceToHost));
+    } else {
+      unsigned long long key = 0;
+      KIE_HIP(hipMemcpy(&key, b.amax, sizeof(key), hipMemcpyDeviceToHost));
+      if (key == 0) return fail(KIE_ERR_BAD_STATE, "the LM-head stage has not run");
+      *static_cast<int32_t*>(out_host) = (int32_t)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
+    }
+    return KIE_OK;
+  }
+  int off = 0, count = 0, slot = 0;
+  bool pair = false;
+  switch (what) {
+    case KIE_ACT_X_ATTN: off = b.off_x; count = c.d_model; slot = kSlotXO; break;
+    case KIE_ACT_X: off = b.off_x; count = c.d_model; slot = kSlotXDown; break;
+    case KIE_ACT_QKV: off = b.off_qkv; count = qd + 2 * kd; slot = kSlotQkv; break;
+    case KIE_ACT_O: off = b.off_o; count = qd; slot = kSlotO; pair = true; break;
+    case KIE_ACT_U: off = b.off_u; count = ucount; slot = kSlotU; pair = true; break;
+    case KIE_ACT_ROUTER:
+      if (!c.n_experts) return fail(KIE_ERR_INVALID_ARG, "a dense model has no router");
+      off = b.off_router; count = c.n_experts; slot = kSlotRouter; break;
+    default: return fail(KIE_ERR_INVALID_ARG, "unknown activation");
+  }
+  if (n < count) return fail(KIE_ERR_INVALID_ARG, "out too small");
+  const int words = pair ? count / 2 : count;
+  std::vector<unsigned long long> w(words);
+  KIE_HIP(hipMemcpy(w.data(), b.act + off, sizeof(unsigned long long) * words, hipMemcpyDeviceToHost));
+  float* out = static_cast<float*>(out_host);
+  const unsigned f = flag(slot);
+  for (int i = 0; i < words; ++i) {
+    const unsigned lo = (unsigned)w[i], hi = (unsigned)(w[i] >> 32);
+    if (pair) {
+      if ((hi >> 16) != f % 65535u + 1u)
+        return fail(KIE_ERR_BAD_STATE, "activation word " + std::to_string(i) + " is not from that stage");
+      const unsigned a = lo & 0xFFFFFFu, bb = (lo >> 24) | ((hi & 0xFFFFu) << 8);
+      unsigned ua = a << 8, ub = bb << 8;
+      std::memcpy(&out[2 * i], &ua, 4);
+      std::memcpy(&out[2 * i + 1], &ub, 4);
+    } else {
+      if (hi != f) return fail(KIE_ERR_BAD_STATE, "activation word " + std::to_string(i) + " is not from that stage");
+      std::memcpy(&out[i], &lo, 4);
+    }
+  }
+  return KIE_OK;
 }
 
 }  // extern "C"

@@ -146,6 +146,29 @@ class Engine:
         check(self.lib.kie_last_elapsed_ms(self.h, ctypes.byref(ms)), "kie_last_elapsed_ms")
         return ms.value
 
+    STAGES = {"qkv": 0, "attention": 1, "o": 2, "gateup": 3, "down": 4, "router": 5, "moe_gateup": 6,
+              "moe_down": 7, "lm_head": 8}
+    ACTS = {"x_attn": 0, "x": 1, "qkv": 2, "o": 3, "u": 4, "router": 5, "logits": 6, "token": 7}
+
+    def debug_stage(self, stage: str, layer: int = 0) -> None:
+        """kie_debug_stage: one stage of the next decode step."""
+        check(self.lib.kie_debug_stage(self.h, self.STAGES[stage], int(layer)), "kie_debug_stage")
+
+    def debug_read_act(self, what: str, layer: int = 0):
+        """kie_debug_read_act: what that stage wrote (float32 array, or the token as int)."""
+        m = self.model
+        sizes = {"x_attn": m.d_model, "x": m.d_model, "qkv": (m.n_heads + 2 * m.n_kv_heads) * m.head_dim,
+                 "o": m.n_heads * m.head_dim,
+                 "u": ((m.top_k + m.n_shared_experts) * m.expert_hidden) if m.n_experts else m.ffn_hidden,
+                 "router": max(1, m.n_experts), "logits": m.vocab_out, "token": 1}
+        if what == "token":
+            out = np.zeros(1, np.int32)
+        else:
+            out = np.zeros(sizes[what], np.float32)
+        check(self.lib.kie_debug_read_act(self.h, self.ACTS[what], int(layer), out.ctypes.data, int(out.size)),
+              "kie_debug_read_act")
+        return int(out[0]) if what == "token" else out
+
     def read_kv(self, layer: int, pos0: int, pos1: int):
         m = self.model
         shape = (m.n_kv_heads, pos1 - pos0, m.head_dim)
