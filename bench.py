@@ -79,10 +79,31 @@ def decode_bytes(c, pos0: int, n: int) -> int:
     return n * W + kv * rows
 
 
+def host_info() -> dict:
+    """CPU model, usable cores and RAM of the host the CPU baseline ran on."""
+    model, mem_kib = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    mem_kib = int(line.split()[1])
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "logical_cpus": os.cpu_count(),
+            "ram_gib": round(mem_kib / 2**20, 1) if mem_kib else None}
+
+
 def cpu_baseline(cfg, W, prompt, budget_s: float):
-    """The oracle as it stands, timed on this host: decode steps after a short
-    batched prefill, until about budget_s seconds of decode have run."""
-    import numpy as np
+    """The oracle as it stands, timed on this host: decode steps after the
+    workload's whole prompt (batched prefill, not timed), until about
+    budget_s seconds of decode have run or the KV capacity is reached."""
     from oracle import Oracle
     from kie_synth import weights_to_numpy
     try:
@@ -90,11 +111,13 @@ def cpu_baseline(cfg, W, prompt, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = None
-    cores = len(os.sched_getaffinity(0))
+    host = host_info()
+    cores = host["affinity_cores"]
     Wn = weights_to_numpy(W)
     o = Oracle(cfg, Wn)
-    p_len = min(64, len(prompt))
-    o.prefill(prompt[:p_len])
+    t_pf = time.perf_counter()
+    o.prefill(prompt)
+    t_pf = time.perf_counter() - t_pf
     o.decode(1)                                 # widens the remaining weights once
     n = 0
     t0 = time.perf_counter()
@@ -104,12 +127,13 @@ def cpu_baseline(cfg, W, prompt, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or o.pos >= cfg.kv_capacity - 1:
             break
-    return {"value": n / el, "unit": "tokens/s", "cores": threads or cores,
+    return {"value": n / el, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"{cfg.name}: numpy fp32 oracle, {n} greedy decode steps after a "
-                       f"{p_len}-token batched prefill ({el:.1f} s on {cores} host cores, "
-                       f"BLAS threads {threads})"),
-            "ms_per_token": 1e3 * el / n}
+            "sample": (f"{cfg.name}: numpy fp32 oracle, {n} greedy decode steps from position "
+                       f"{len(prompt) + 1} after the {len(prompt)}-token prompt's batched prefill "
+                       f"({t_pf:.1f} s, not timed); {el:.1f} s of decode on {cores} usable host "
+                       f"cores, BLAS threads {threads}"),
+            "ms_per_token": 1e3 * el / n, "blas_threads": threads, "host": host}
 
 
 def trace_summary(cfg, tr):
@@ -140,31 +164,62 @@ def trace_summary(cfg, tr):
             d[key + "_mean_us"] = d.get(key + "_mean_us", 0.0) + float(v.mean())
             d[key + "_max_us"] = d.get(key + "_max_us", 0.0) + float(v.max())
         prev_end = end
+    tot = {k: sum(d.get(k + "_mean_us", 0.0) for d in out.values()) for k in ("wait", "prep", "work")}
     for d in out.values():
         for key in list(d):
             if key != "n":
                 d[key] /= d["n"]
-    return {"step_us": float(t[:, -1].max()), "stages": out}
+    step = float(t[:, -1].max())
+    # per step, averaged over workgroups: the time spent waiting for a
+    # stage's inputs (the exchange and the step barrier) against the whole
+    return {"step_us": step, "wait_us": tot["wait"], "prep_us": tot["prep"],
+            "work_us": tot["work"], "idle_frac": tot["wait"] / step if step > 0 else None,
+            "stages": out}
 
 
-def hbm_probes(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 10) -> dict:
+def hbm_probes(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 10,
+               sweep: bool = True) -> dict:
     """Achievable HBM streaming rates on this device, from the library's
     plain streaming kernel: a read-only pass over ``read_bytes`` and a copy
-    of ``copy_bytes`` (reads + writes counted)."""
+    of ``copy_bytes`` (reads + writes counted), in the default shape (8
+    non-temporal global loads in flight per lane, four workgroups per
+    compute unit); with ``sweep`` also every load kind x loads in flight x
+    workgroups per compute unit, whose best read rate is the ceiling the
+    decode kernel is judged against."""
     import torch
     import persistent_decode_monokernel_amd as kie
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     src = torch.empty(read_bytes // 2, dtype=torch.float16, device="cuda")
     src.fill_(1.0)
     kie.debug_stream(src, None, reps=2)
     ms_r = kie.debug_stream(src, None, reps=reps)
+    out = {"read_gbs": read_bytes / (ms_r * 1e-3) / 1e9, "read_bytes": read_bytes,
+           "read_ms": ms_r, "kernel": "kie::stream_kernel", "n_cu": n_cu}
+    if sweep:
+        pts = []
+        for kind in (0, 1, 2):
+            for depth in (2, 4, 8, 16):
+                for per_cu in (1, 2, 4, 8):
+                    kie.debug_stream(src, None, n_workgroups=per_cu * n_cu, reps=1, depth=depth,
+                                     kind=kind)
+                    ms = kie.debug_stream(src, None, n_workgroups=per_cu * n_cu, reps=5,
+                                          depth=depth, kind=kind)
+                    pts.append([kind, depth, per_cu, round(read_bytes / (ms * 1e-3) / 1e9, 1)])
+        best = max(pts, key=lambda q: q[3])
+        out.update({"read_best_gbs": best[3],
+                    "read_best_shape": {"kind": ["global_nt", "global", "buffer_nt"][best[0]],
+                                        "loads_in_flight": best[1], "wg_per_cu": best[2]},
+                    "sweep_cols": ["kind(0 global nt,1 global,2 buffer nt)", "loads_in_flight",
+                                   "wg_per_cu", "GB/s"],
+                    "sweep": pts})
     a = src[: copy_bytes // 2]
     dst = torch.empty_like(a)
     kie.debug_stream(a, dst, reps=2)
     ms_c = kie.debug_stream(a, dst, reps=reps)
+    out.update({"copy_gbs": 2 * copy_bytes / (ms_c * 1e-3) / 1e9, "copy_bytes": copy_bytes,
+                "copy_ms": ms_c})
     del src, dst
-    return {"read_gbs": read_bytes / (ms_r * 1e-3) / 1e9, "read_bytes": read_bytes,
-            "copy_gbs": 2 * copy_bytes / (ms_c * 1e-3) / 1e9, "copy_bytes": copy_bytes,
-            "read_ms": ms_r, "copy_ms": ms_c, "kernel": "kie::stream_kernel"}
+    return out
 
 
 def main(argv=None):
@@ -178,8 +233,15 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming probes")
-    ap.add_argument("--trace", action="store_true",
-                    help="also run one traced decode and add a per-stage breakdown to detail")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the traced decode whose per-stage wait/work breakdown and idle "
+                         "fraction go into detail.trace")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the extra decode over the workload's whole length when --steps "
+                         "is shorter")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip the persistent vs staged-hipGraph comparison")
+    ap.add_argument("--no-sweep", action="store_true", help="only the default streaming probe shape")
     ap.add_argument("--cooperative", action="store_true",
                     help="launch the persistent kernel as a cooperative dispatch (the default is "
                          "an ordinary dispatch, which profilers can trace; residency of every "
@@ -201,7 +263,7 @@ def main(argv=None):
 
     if args.probe_only:
         torch.cuda.set_device(0)
-        print(json.dumps({"probe": hbm_probes()}), flush=True)
+        print(json.dumps({"probe": hbm_probes(sweep=not args.no_sweep)}), flush=True)
         return 0
 
     cfg = get_config(args.config)
@@ -214,31 +276,49 @@ def main(argv=None):
     prompt = make_prompt(cfg, seed=0)
     stream = torch.cuda.current_stream()
 
-    eng = kie.Engine(cfg, W, max_seq=max_seq, graph=args.graph, plain_launch=not args.cooperative)
-    eng.prefill(prompt)
-    if args.warmup:
-        eng.decode(args.warmup, logits=False)
-    toks = torch.empty(K, dtype=torch.int32, device=dev)
-    times, kernel_ms, prefill_ms = [], [], []
-    for _ in range(max(1, args.reps)):
-        eng.reset()
-        eng.prefill(prompt)
-        prefill_ms.append(eng.last_elapsed_ms())
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        eng.decode_into(K, toks, None)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-        kernel_ms.append(eng.last_elapsed_ms())
-    med = sorted(range(len(times)), key=lambda i: times[i])[len(times) // 2]
-    ms = times[med]
-    kms = kernel_ms[med]
+    def timed(engine, n, reps):
+        """Median over reps of one n-step decode call after a fresh prefill:
+        (call ms from events on the engine's stream, kernel ms, prefill ms)."""
+        toks = torch.empty(n, dtype=torch.int32, device=dev)
+        rows = []
+        for _ in range(max(1, reps)):
+            engine.reset()
+            engine.prefill(prompt)
+            pf = engine.last_elapsed_ms()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            engine.decode_into(n, toks, None)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rows.append((e0.elapsed_time(e1), engine.last_elapsed_ms(), pf))
+        rows.sort()
+        return rows[len(rows) // 2], [r[0] for r in rows]
+
+    def make_engine(graph, trace=False):
+        e = kie.Engine(cfg, W, max_seq=max_seq, graph=graph, trace=trace,
+                       plain_launch=not args.cooperative)
+        e.prefill(prompt)
+        if args.warmup:
+            e.decode(args.warmup, logits=False)
+        return e
+
+    eng = make_engine(args.graph)
+    (ms, kms, pf_ms), times = timed(eng, K, args.reps)
     tok_s = K / (ms / 1e3)
     nbytes = decode_bytes(cfg, P - 1, K)
     achieved = nbytes / (kms / 1e3) / 1e9
+    # the workload's whole decode length as well, when the timed K is shorter
+    Kf = cfg.n_decode
+    full = None
+    if K != Kf and not args.no_full:
+        (f_ms, f_kms, _), _ = timed(eng, Kf, args.reps)
+        fb = decode_bytes(cfg, P - 1, Kf)
+        full = {"steps": Kf, "ms_per_token": f_ms / Kf, "tok_s": Kf / (f_ms / 1e3),
+                "kernel_ms": f_kms, "bytes": fb, "achieved_gbs": fb / (f_kms / 1e3) / 1e9,
+                "frac": fb / (f_kms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "traffic": measured_traffic(cfg, P - 1, Kf)}
     # the prompt through the batched (matrix-core) prefill instead: not part
     # of the decode metric, reported beside the persistent kernel's prefill
     batched_ms = None
@@ -249,15 +329,41 @@ def main(argv=None):
         eng.prefill_batched(prompt)
         batched_ms = eng.last_elapsed_ms()
     eng.close()
+    # persistent kernel against the same step as one launch per stage,
+    # replayed from a captured hipGraph: the cost of launching and ending a
+    # kernel per stage instead of waiting on flags inside one
+    ab = None
+    if not args.no_ab:
+        n_ab = Kf
+        other = make_engine(not args.graph)
+        (o_ms, o_kms, _), _ = timed(other, n_ab, args.reps)
+        other.close()
+        if full is not None or K == n_ab:
+            mine = full["ms_per_token"] if full is not None else ms / K
+        else:
+            mine = None
+        pers, graph = (o_ms / n_ab, mine) if args.graph else (mine, o_ms / n_ab)
+        splits = max(1, max(cfg.n_kv_heads, torch.cuda.get_device_properties(0).multi_processor_count)
+                     // cfg.n_kv_heads)
+        per_layer = (6 if cfg.n_experts else 5) + (1 if splits > 1 else 0)
+        launches = cfg.n_layers * per_layer + 2
+        ab = {"steps": n_ab, "persistent_ms_per_token": pers, "graph_ms_per_token": graph,
+              "graph_launches_per_token": launches,
+              "extra_us_per_launch": (1e3 * (graph - pers) / launches
+                                      if pers is not None and graph is not None else None)}
     trace = None
-    if args.trace and not args.graph:
-        te = kie.Engine(cfg, W, max_seq=max_seq, trace=True, plain_launch=not args.cooperative)
+    if not args.no_trace and not args.graph:
+        te = make_engine(False, trace=True)
+        toks = torch.empty(8, dtype=torch.int32, device=dev)
+        te.reset()
         te.prefill(prompt)
-        te.decode_into(min(K, 8), toks, None)
+        te.decode_into(8, toks, None)
         trace = trace_summary(cfg, te.read_trace())
+        trace["note"] = ("step 1 of an 8-step decode after the prompt, from the in-kernel "
+                         "stamps; wait = inputs-complete minus the workgroup's previous stage "
+                         "end, summed over the step's stages and averaged over workgroups")
         te.close()
-    probes = None if args.no_probe else hbm_probes()
-
+    probes = None if args.no_probe else hbm_probes(sweep=not args.no_sweep)
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -286,12 +392,14 @@ def main(argv=None):
         "detail": {"kernel": "kie::mono_kernel" if not args.graph else "kie::stage_kernel",
                    "bytes_per_launch": nbytes, "bytes_per_token": nbytes / K,
                    "kernel_ms": kms, "call_ms": ms, "reps_call_ms": times,
+                   "full_decode": full, "graph_ab": ab,
                    "roofline_tok_s": HBM_PEAK_GBS * 1e9 / (nbytes / K),
                    "hbm_probe": probes,
-                   "frac_of_read_probe": (achieved / probes["read_gbs"]) if probes else None,
+                   "frac_of_read_probe": (achieved / probes.get("read_best_gbs", probes["read_gbs"])
+                                          if probes else None),
                    "trace": trace,
                    "prefill": {"positions": P - 1,
-                               "persistent_ms": sorted(prefill_ms)[len(prefill_ms) // 2],
+                               "persistent_ms": pf_ms,
                                "batched_ms": batched_ms}},
         "cpu_baseline": None,
     }

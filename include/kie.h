@@ -77,8 +77,8 @@ typedef enum kie_status {
 #define KIE_TRACE 0x2u        /* persistent mode: record, for one decode step
                                  of every kie_decode call (step 1, or step 0
                                  of a one-step call), each workgroup's clock
-                                 (100 MHz wall clock) when it arrives at and
-                                 leaves every grid barrier; read it back with
+                                 (100 MHz wall clock) at the step's start and
+                                 three times per stage; read it back with
                                  kie_debug_read_trace.  Results are unchanged. */
 #define KIE_PLAIN_LAUNCH 0x4u /* persistent mode: launch with an ordinary
                                  dispatch instead of the cooperative-launch API
@@ -354,8 +354,11 @@ int kie_debug_barrier(int32_t n_workgroups, int32_t n_rounds, int32_t spin_limit
 /* KIE_TRACE handles: copies the trace of the last kie_decode call to
  * `out` (host, uint64 [n_workgroups][max_events]) and sets *n_events to the
  * number of events each workgroup recorded: event 0 is the start of the
- * traced step, then for every grid barrier of that step one event when the
- * workgroup arrives and one when it leaves.  KIE_ERR_BAD_STATE without
+ * traced step, then three events for every stage of that step in execution
+ * order (per layer Q/K/V, attention, O, then gate/up and down, or router,
+ * expert gate/up and expert down; then lm_head): when the stage's inputs
+ * were complete, when its main loop started (after the norm, or after RoPE
+ * and the KV append) and when it ended.  KIE_ERR_BAD_STATE without
  * KIE_TRACE or before a decode call; KIE_ERR_INVALID_ARG if max_events is
  * smaller than the recorded count. */
 int kie_debug_read_trace(const kie_handle *h, uint64_t *out, int32_t max_events,
@@ -371,6 +374,19 @@ int kie_debug_read_trace(const kie_handle *h, uint64_t *out, int32_t max_events,
  * are calibrated. */
 int kie_debug_stream(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
                      int32_t reps, float *ms_per_launch, void *hip_stream);
+
+/* The streaming probe with its shape chosen: `depth` (1, 2, 4, 8 or 16)
+ * 128-bit loads in flight per lane, and `kind` the load: 0 non-temporal
+ * global loads (what kie_debug_stream uses, with depth 8), 1 plain global
+ * loads, 2 the raw buffer loads with the non-temporal policy that the
+ * decode kernel streams its weights with (bytes below 4 GiB).  Other
+ * arguments and errors as kie_debug_stream; KIE_ERR_INVALID_ARG for another
+ * depth or kind.  A sweep over depth, kind and n_workgroups gives the
+ * read rate this device reaches at all, the ceiling against which the
+ * decode kernel's streaming is judged. */
+int kie_debug_stream_ex(const void *src, void *dst, size_t bytes, int32_t n_workgroups,
+                        int32_t depth, int32_t kind, int32_t reps, float *ms_per_launch,
+                        void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -92,6 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_debug_barrier": (ctypes.c_int, [I32, I32, I32, P(I32), P(ctypes.c_float), VP]),
         "kie_debug_read_trace": (ctypes.c_int, [VP, P(ctypes.c_uint64), I32, P(I32), P(I32)]),
         "kie_debug_stream": (ctypes.c_int, [VP, VP, ctypes.c_size_t, I32, I32, P(ctypes.c_float), VP]),
+        "kie_debug_stream_ex": (ctypes.c_int, [VP, VP, ctypes.c_size_t, I32, I32, I32, I32,
+                                               P(ctypes.c_float), VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -623,24 +623,35 @@ __device__ __forceinline__ void gather_take(GatherSlots& S, const u32x2 (&v)[kGa
   }
 }
 
+// Bookkeeping of one poll round: false (with the timeout reported) once the
+// wait has passed its time limit or spin limit, or another workgroup has
+// reported an error.
+__device__ __forceinline__ bool poll_check(const Ctl& c, int& spins, long long& t0) {
+  ++spins;
+  if ((spins & 15) == 1) {
+    if (spins == 1) t0 = wall_clock64();
+    if (__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if (wall_clock64() - t0 > c.ticks) {
+      set_timeout(c.err);
+      return false;
+    }
+  }
+  if (c.spin_limit > 0 && spins >= c.spin_limit) {
+    set_timeout(c.err);
+    return false;
+  }
+  return true;
+}
+
 // Polls until every slot is valid; false on timeout or a reported error.
+// One poll round per return: a second round in flight, or a longer pause
+// between rounds, both measured slower (more poll traffic delays the data's
+// own propagation; a pause delays its detection).
 __device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherSlots& S, const Ctl& c) {
   long long t0 = 0;
   int spins = 0;
   while (S.pending) {
-    ++spins;
-    if ((spins & 15) == 1) {
-      if (spins == 1) t0 = wall_clock64();
-      if (__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
-      if (wall_clock64() - t0 > c.ticks) {
-        set_timeout(c.err);
-        return false;
-      }
-    }
-    if (c.spin_limit > 0 && spins >= c.spin_limit) {
-      set_timeout(c.err);
-      return false;
-    }
+    if (!poll_check(c, spins, t0)) return false;
     __builtin_amdgcn_s_sleep(1);
     u32x2 v[kGatherPer];
     gather_issue(arena, S, v);
@@ -2153,22 +2164,33 @@ __global__ __launch_bounds__(kThreads, 1) void barrier_test_kernel(unsigned* bar
   if (threadIdx.x == 0 && bad) atomicAdd(violations, bad);
 }
 
-// Plain HBM streaming probe: reads n16 16-byte words (grid-stride, 8 loads
-// in flight per lane) and either copies them to dst or folds them into a
-// value that is stored only if it equals an arbitrary constant (so the reads
-// cannot be dropped).  Gives the achievable read bandwidth of the device and
-// a copy of known size for calibrating the memory counters.
+// Plain HBM streaming probe: reads n16 16-byte words grid-stride with kU
+// loads in flight per lane and either copies them to dst or folds them into
+// a value that is stored only if it equals an arbitrary constant (so the
+// reads cannot be dropped).  kKind picks the load: 0 a non-temporal global
+// load, 1 a plain global load, 2 the raw buffer load with the non-temporal
+// policy that the decode kernel streams its weights with.  Gives the
+// achievable read bandwidth of the device and a copy of known size for
+// calibrating the memory counters.
+template <int kKind>
+__device__ __forceinline__ u32x4 stream_ld(const u32x4* src, Rsrc r, size_t i) {
+  if constexpr (kKind == 0) return __builtin_nontemporal_load(src + i);
+  else if constexpr (kKind == 1) return src[i];
+  else return ld_w16(r, (unsigned)(i * 16u));
+}
+
+template <int kU, int kKind>
 __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4* __restrict__ src,
                                                           u32x4* __restrict__ dst, size_t n16,
                                                           unsigned* sink) {
-  constexpr int kU = 8;
+  const Rsrc r = make_rsrc(src, kKind == 2 ? n16 * 16u : 16u);
   const size_t stride = (size_t)gridDim.x * kThreads;
   size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (; i + (kU - 1) * stride < n16; i += kU * stride) {
     u32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kU; ++u) v[u] = stream_ld<kKind>(src, r, i + u * stride);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (dst) dst[i + u * stride] = v[u];
@@ -2176,7 +2198,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4* __restric
     }
   }
   for (; i < n16; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(src + i);
+    const u32x4 v = stream_ld<kKind>(src, r, i);
     if (dst) dst[i] = v;
     else acc ^= v;
   }
@@ -2262,11 +2284,24 @@ hipError_t launch_barrier_test(unsigned* bar, unsigned* slots, int* violations, 
                                     dim3(n_wg), dim3(kThreads), args, 0u, s);
 }
 
-hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, unsigned* sink,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(stream_kernel, dim3(n_wg), dim3(kThreads), 0, s,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16, sink);
-  return hipGetLastError();
+template <int kKind>
+static const void* stream_for(int depth) {
+  switch (depth) {
+    case 1: return reinterpret_cast<const void*>(stream_kernel<1, kKind>);
+    case 2: return reinterpret_cast<const void*>(stream_kernel<2, kKind>);
+    case 4: return reinterpret_cast<const void*>(stream_kernel<4, kKind>);
+    case 16: return reinterpret_cast<const void*>(stream_kernel<16, kKind>);
+    default: return reinterpret_cast<const void*>(stream_kernel<8, kKind>);
+  }
+}
+
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, int depth, int kind,
+                         unsigned* sink, hipStream_t s) {
+  const void* k = kind == 1 ? stream_for<1>(depth) : kind == 2 ? stream_for<2>(depth)
+                                                               : stream_for<0>(depth);
+  size_t n16 = bytes / 16;
+  void* args[] = {&src, &dst, &n16, &sink};
+  return hipLaunchKernel(k, dim3(n_wg), dim3(kThreads), args, 0u, s);
 }
 
 }  // namespace kie

@@ -103,8 +103,10 @@ size_t gemv_lds_bytes(int cols);
 hipError_t launch_barrier_test(unsigned* bar, unsigned* slots, int* violations, int* err, int n_wg,
                                int rounds, long long timeout_ticks, int spin_limit,
                                hipStream_t s);
-hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, unsigned* sink,
-                         hipStream_t s);
+// kind: 0 non-temporal global loads, 1 plain global loads, 2 the decode
+// kernel's non-temporal buffer loads (bytes < 4 GiB); depth 1, 2, 4, 8 or 16
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, int n_wg, int depth, int kind,
+                         unsigned* sink, hipStream_t s);
 // Batched prefill (kie_prefill.hip)
 hipError_t launch_split(const float* x, int ldx, __half* hi, __half* lo, int M, int K, hipStream_t s);
 hipError_t launch_gemm(const __half* ahi, const __half* alo, int lda, const __half* w, int ldw, float* c,

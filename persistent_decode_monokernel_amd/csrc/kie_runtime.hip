@@ -1071,9 +1071,19 @@ int kie_debug_barrier(int32_t n_wg, int32_t rounds, int32_t spin_limit, int32_t*
 
 int kie_debug_stream(const void* src, void* dst, size_t bytes, int32_t n_wg, int32_t reps,
                      float* ms_per_launch, void* hip_stream) {
+  return kie_debug_stream_ex(src, dst, bytes, n_wg, 8, 0, reps, ms_per_launch, hip_stream);
+}
+
+int kie_debug_stream_ex(const void* src, void* dst, size_t bytes, int32_t n_wg, int32_t depth,
+                        int32_t kind, int32_t reps, float* ms_per_launch, void* hip_stream) {
   g_err.clear();
   if (bytes == 0 || bytes % 16 != 0 || reps < 1 || reps > 10000 || n_wg < 0 || n_wg > 65536)
     return fail(KIE_ERR_INVALID_ARG, "need bytes a positive multiple of 16, 1 <= reps <= 10000");
+  if (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)
+    return fail(KIE_ERR_INVALID_ARG, "depth must be 1, 2, 4, 8 or 16");
+  if (kind < 0 || kind > 2) return fail(KIE_ERR_INVALID_ARG, "kind must be 0, 1 or 2");
+  if (kind == 2 && bytes >= (size_t(1) << 32))
+    return fail(KIE_ERR_INVALID_ARG, "buffer loads (kind 2) address less than 4 GiB");
   int rc;
   if ((rc = check_device_range(src, bytes, "src"))) return rc;
   if (dst && (rc = check_device_range(dst, bytes, "dst"))) return rc;
@@ -1093,7 +1103,7 @@ int kie_debug_stream(const void* src, void* dst, size_t bytes, int32_t n_wg, int
     }
     hipError_t e = hipSuccess;
     for (int r = 0; r < reps && e == hipSuccess; ++r)
-      e = kie::launch_stream(src, dst, bytes, grid, static_cast<unsigned*>(sink), s);
+      e = kie::launch_stream(src, dst, bytes, grid, depth, kind, static_cast<unsigned*>(sink), s);
     float ms = 0.f;
     if (e != hipSuccess || hipEventRecord(e1, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {

@@ -255,17 +255,20 @@ def debug_barrier(n_workgroups: int = 0, rounds: int = 1000, spin_limit: int = 0
 
 
 def debug_stream(src: torch.Tensor, dst: Optional[torch.Tensor] = None, n_workgroups: int = 0,
-                 reps: int = 10) -> float:
-    """HBM streaming probe: ms per launch to read ``src`` (and copy it to ``dst``)."""
+                 reps: int = 10, depth: int = 8, kind: int = 0) -> float:
+    """HBM streaming probe: ms per launch to read ``src`` (and copy it to
+    ``dst``) with ``depth`` 128-bit loads in flight per lane; ``kind`` 0 is a
+    non-temporal global load, 1 a plain global load, 2 the decode kernel's
+    non-temporal buffer load."""
     lib = _lib.load()
     ms = ctypes.c_float()
     s = torch.cuda.current_stream()
     nbytes = src.numel() * src.element_size()
     if dst is not None and dst.numel() * dst.element_size() != nbytes:
         raise ValueError("dst must have the size of src")
-    check(lib.kie_debug_stream(src.data_ptr(), dst.data_ptr() if dst is not None else None,
-                               nbytes, n_workgroups, reps, ctypes.byref(ms),
-                               ctypes.c_void_p(s.cuda_stream)), "kie_debug_stream")
+    check(lib.kie_debug_stream_ex(src.data_ptr(), dst.data_ptr() if dst is not None else None,
+                                  nbytes, n_workgroups, depth, kind, reps, ctypes.byref(ms),
+                                  ctypes.c_void_p(s.cuda_stream)), "kie_debug_stream_ex")
     return ms.value
 
 

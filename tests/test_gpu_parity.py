@@ -60,6 +60,29 @@ def test_gemv_stage_matches_float64(torch, kie, rows, cols):
         assert np.all(np.abs(y - want) <= 1e-5 * scale + 1e-30), float(np.max(np.abs(y - want) / scale))
 
 
+# ---------------------------------------------------------------- streaming probe
+def test_stream_probe_copies_exactly_in_every_shape(torch, kie):
+    # the probe is what the memory counters are calibrated on and what the
+    # decode kernel's streaming is compared against: every load depth and
+    # kind must move every byte, including a tail that is not a whole
+    # grid-stride pass
+    _say("stream probe shapes")
+    n16 = 3 * 512 * 8 * 37 + 5
+    g = torch.Generator(device="cuda").manual_seed(7)
+    src = torch.randint(-2**31, 2**31 - 1, (n16 * 4,), dtype=torch.int32, device="cuda", generator=g)
+    for kind in (0, 1, 2):
+        for depth in (1, 2, 4, 8, 16):
+            dst = torch.zeros_like(src)
+            kie.debug_stream(src, dst, n_workgroups=37, reps=1, depth=depth, kind=kind)
+            torch.cuda.synchronize()
+            assert torch.equal(dst, src), (kind, depth)
+            assert kie.debug_stream(src, None, n_workgroups=37, reps=1, depth=depth, kind=kind) > 0
+    with pytest.raises(kie.KieError):
+        kie.debug_stream(src, None, depth=3)
+    with pytest.raises(kie.KieError):
+        kie.debug_stream(src, None, kind=3)
+
+
 # ---------------------------------------------------------------- barrier
 def test_grid_barrier_stress(torch, kie):
     _say("barrier stress")
