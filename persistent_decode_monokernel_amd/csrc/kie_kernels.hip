@@ -882,6 +882,19 @@ struct MoePairAddr {         // virtual row 2f (+1): pair f = (slot f / Fe, row 
     return ((unsigned)ids[a] * (unsigned)Fe + (unsigned)ff) * (unsigned)d * 2u + (unsigned)c * 16u;
   }
 };
+struct MoeSharedPairAddr {   // as MoePairAddr over the shared experts only: pair f = (shared f / Fe, row f % Fe)
+  unsigned long long bg, bu;
+  int E, ne, Fe, d;
+  __device__ Rsrc rsrc(int vr) const {
+    const unsigned long long iu = vr & 1;
+    return make_rsrc(reinterpret_cast<const void*>((1ull - iu) * bg + iu * bu), (size_t)ne * Fe * d * 2);
+  }
+  __device__ unsigned off(int vr, int c) const {
+    const int f = vr >> 1;
+    const int a = f / Fe, ff = f - a * Fe;
+    return ((unsigned)(E + a) * (unsigned)Fe + (unsigned)ff) * (unsigned)d * 2u + (unsigned)c * 16u;
+  }
+};
 struct MoeDownAddr {         // row r of the concatenated active experts' down rows
   Rsrc down;                 // whole stacked tensor [E + S][d][Fe]
   const int* ids;
@@ -1613,35 +1626,58 @@ __device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wt
 __device__ __forceinline__ int* moe_ids(Lds s) { return reinterpret_cast<int*>(s.red + kRedIdsOff); }
 __device__ __forceinline__ float* moe_wts(Lds s) { return s.red + kRedWtsOff; }
 
-__device__ __forceinline__ GemvWork moe_gu_work(const Params& p, int wg) {
-  return gemv_work(2 * (p.topk + p.nshared) * p.Fe, p.d, p.n_wg, wg, 4);
+// The gate/up rows of the active experts are dealt out in two parts: the
+// shared experts' rows, which do not depend on the routing, and the routed
+// experts' rows.  Every workgroup streams its share of the shared rows first
+// (their first batches issued behind the poll for x), so the router logits'
+// hand-off and the routing overlap weight streaming instead of stalling it.
+// The routed part is dealt in reverse workgroup order so that the workgroups
+// holding an extra unit of one part do not also hold one of the other.
+__device__ __forceinline__ GemvWork moe_gu_shared_work(const Params& p, int wg) {
+  return gemv_work(2 * p.nshared * p.Fe, p.d, p.n_wg, wg, 4);
+}
+__device__ __forceinline__ GemvWork moe_gu_routed_work(const Params& p, int wg) {
+  return gemv_work(2 * p.topk * p.Fe, p.d, p.n_wg, p.n_wg - 1 - wg, 4);
 }
 __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int l, int wg, Lds s,
                                                  const Ctl& c, Tracer& tr) {
   const LayerPtrs w = layer(p, l);
   int* ids = moe_ids(s);
   float* wts = moe_wts(s);
-  const GemvWork g = moe_gu_work(p, wg);
+  const GemvWork gs = moe_gu_shared_work(p, wg);
+  const GemvWork gr = moe_gu_routed_work(p, wg);
+  const int Fe = p.Fe, K = p.topk, ne = p.E + p.nshared;
+  const MoeSharedPairAddr saddr{uniform_addr(w.e_gate), uniform_addr(w.e_up), p.E, ne, Fe, p.d};
   const __half* gain = w.ffn_norm;
   const GainPre G = gain_prefetch(gain, p.d);
-  const bool rows = g.r0 < g.r1;
-  const LLRange rg[2] = {{p.off_router, p.E, s.sums, ll_flag(p, step, l, kSlotRouter)},
-                         {p.off_x, rows ? p.d : 0, s.h, ll_flag(p, step, l, kSlotXO)}};
-  if (!ll_gather(p, rg, c)) return false;
+  const bool srows = gs.r0 < gs.r1;
+  const bool rows = srows || gr.r0 < gr.r1;
+  WPre pre = {};
+  const LLRange rx[1] = {{p.off_x, rows ? p.d : 0, s.h, ll_flag(p, step, l, kSlotXO)}};
+  if (!ll_gather_pf(p, rx, c, [] {}, [&]() {
+        if (srows) pre = gemv_prefetch(gs, saddr);
+      }))
+    return false;
   mark(tr);
-  moe_routing(p, ids, wts, s.sums);
-  if (wg == 0 && threadIdx.x < p.topk)
-    p.expert_log[((size_t)(p.pos0 + step) * p.L + l) * p.topk + threadIdx.x] = ids[threadIdx.x];
-  if (!rows) {
-    mark(tr);
-    return true;
-  }
-  const float inv = rmsnorm_lds(p, gain, G, s.h, s.red);
+  const float inv = rows ? rmsnorm_lds(p, gain, G, s.h, s.red) : 0.f;
   mark(tr);
-  const int Fe = p.Fe, ne = p.E + p.nshared;
-  const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
   const unsigned f = ll_flag(p, step, l, kSlotU);
-  gemv_run<false>(g, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
+  // u of the shared experts (routing weight 1): slots K, K + 1, ...
+  gemv_run<true>(gs, saddr, s.h, s.part, s.sums, pre, [&](int b0, int n, const float* sums) {
+    for (int j = threadIdx.x; 4 * j < n; j += kThreads) {
+      const int ff = K * Fe + (b0 >> 1) + 2 * j;
+      ll_put2(p, p.off_u + (ff >> 1), silu(sums[4 * j] * inv) * (sums[4 * j + 1] * inv),
+              silu(sums[4 * j + 2] * inv) * (sums[4 * j + 3] * inv), f);
+    }
+  });
+  __syncthreads();
+  const LLRange rl[1] = {{p.off_router, p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
+  if (!ll_gather(p, rl, c)) return false;
+  moe_routing(p, ids, wts, s.sums);
+  if (wg == 0 && threadIdx.x < K)
+    p.expert_log[((size_t)(p.pos0 + step) * p.L + l) * K + threadIdx.x] = ids[threadIdx.x];
+  const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
+  gemv_run<false>(gr, addr, s.h, s.part, s.sums, WPre{}, [&](int b0, int n, const float* sums) {
     for (int j = threadIdx.x; 4 * j < n; j += kThreads) {     // u[ff], u[ff + 1]
       const int ff = (b0 >> 1) + 2 * j;
       ll_put2(p, p.off_u + (ff >> 1),
