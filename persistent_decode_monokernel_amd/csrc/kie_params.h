@@ -124,6 +124,11 @@ hipError_t launch_attn_prefill(const float* QKV, int ldq, const __half* kc, cons
                                int nkv, int hd, int pos0, float* O, int T, hipStream_t s);
 hipError_t launch_swiglu_split(const float* G, const float* U, size_t n, __half* hi, __half* lo,
                                hipStream_t s);
+// Groups `rows` compact rows by expert on the device: fill (int[E]) and
+// tiles (int[3 * max_tiles]) are workspace; perm/inv as the grouped products
+// and the combine read them.  E must be at most 1024.
+hipError_t launch_moe_group(const int* ids, int rows, int E, int* fill, int* tiles, int max_tiles, int* perm,
+                            int* inv, hipStream_t s);
 hipError_t launch_route(const float* R, int E, int topk, int renorm, int* ids, float* wts, int* log, int L, int l,
                         int pos0, int T, hipStream_t s);
 hipError_t launch_gather_rows(const __half* hi, const __half* lo, int d, const int* perm, int topk, __half* ch,

@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const __half* __restrict__ ah
   if (tiles) {
     m0 = tiles[3 * blockIdx.y];
     M = tiles[3 * blockIdx.y + 1];
+    if (m0 >= M) return;                  // an unused tile slot (the grid covers the most there can be)
     w += (size_t)tiles[3 * blockIdx.y + 2] * wstride;
   }
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32 * WN;
@@ -550,6 +551,76 @@ __global__ __launch_bounds__(kPT) void combine_kernel(float* __restrict__ X, int
     for (int a = 0; a < topk; ++a) v += Y[(size_t)inv[t * topk + a] * d + i];
     X[(size_t)t * d + i] += v;
   }
+}
+
+// Groups the compact rows by expert on the device.  moe_group_kernel (one
+// block) counts the rows of each expert, places each expert's rows at the
+// exclusive prefix sum of the counts (fill[e] = first row of expert e) and
+// writes the row tiles: expert e's rows in tiles of at most 64, in expert
+// order, and every tile slot past the last one empty.  moe_scatter_kernel
+// then gives each row i its compact row q by an atomic increment of its
+// expert's fill.  The order of rows within an expert is not fixed, but no
+// result depends on it: each compact row's products are computed on their
+// own, and the combine sums a position's experts in rank order.
+constexpr int kGroupThreads = 1024;
+__global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int* __restrict__ ids, int rows, int E,
+                                                                 int* __restrict__ fill, int* __restrict__ tiles,
+                                                                 int max_tiles) {
+  __shared__ int cnt[kGroupThreads], off[kGroupThreads], toff[kGroupThreads];
+  const int t = threadIdx.x;
+  cnt[t] = 0;
+  __syncthreads();
+  for (int i = t; i < rows; i += kGroupThreads) atomicAdd(&cnt[ids[i]], 1);
+  __syncthreads();
+  const int c = t < E ? cnt[t] : 0;
+  const int tc = (c + 63) / 64;
+  off[t] = c;
+  toff[t] = tc;
+  __syncthreads();
+  for (int o = 1; o < kGroupThreads; o <<= 1) {       // inclusive scans of counts and tile counts
+    const int a = t >= o ? off[t - o] : 0;
+    const int b = t >= o ? toff[t - o] : 0;
+    __syncthreads();
+    off[t] += a;
+    toff[t] += b;
+    __syncthreads();
+  }
+  const int r0 = off[t] - c, y0 = toff[t] - tc;
+  if (t < E) {
+    fill[t] = r0;
+    for (int j = 0; j < tc; ++j) {
+      const int y = y0 + j;
+      tiles[3 * y] = r0 + 64 * j;
+      tiles[3 * y + 1] = min(r0 + 64 * (j + 1), r0 + c);
+      tiles[3 * y + 2] = t;
+    }
+  }
+  for (int y = toff[kGroupThreads - 1] + t; y < max_tiles; y += kGroupThreads) {
+    tiles[3 * y] = 0;
+    tiles[3 * y + 1] = 0;
+    tiles[3 * y + 2] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kPT) void moe_scatter_kernel(const int* __restrict__ ids, int rows,
+                                                          int* __restrict__ fill, int* __restrict__ perm,
+                                                          int* __restrict__ inv) {
+  const int i = blockIdx.x * kPT + threadIdx.x;
+  if (i < rows) {
+    const int q = atomicAdd(&fill[ids[i]], 1);
+    perm[q] = i;
+    inv[i] = q;
+  }
+}
+
+hipError_t launch_moe_group(const int* ids, int rows, int E, int* fill, int* tiles, int max_tiles, int* perm,
+                            int* inv, hipStream_t s) {
+  if (E > kGroupThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, ids, rows, E, fill, tiles, max_tiles);
+  if (rows > 0)
+    hipLaunchKernelGGL(moe_scatter_kernel, dim3((rows + kPT - 1) / kPT), dim3(kPT), 0, s, ids, rows, fill, perm,
+                       inv);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const float* R, int E, int topk, int renorm, int* ids, float* wts, int* log, int L, int l,

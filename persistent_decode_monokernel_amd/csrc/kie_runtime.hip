@@ -113,7 +113,6 @@ struct kie_handle {
   size_t pf_ws_bytes = 0;
   // MoE batched prefill: host copies of one chunk's routing and grouping,
   // sized at creation for the largest chunk
-  std::vector<int> moe_ids, moe_perm, moe_inv, moe_tiles, moe_off, moe_fill;
 };
 
 namespace {
@@ -439,16 +438,6 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
     return bail(fail(KIE_ERR_HIP, "initialising handle buffers failed"));
   const int tmo = c.timeout_ms > 0 ? c.timeout_ms : 20000;
   p.timeout_ticks = (long long)tmo * h->ticks_per_ms;
-  if (c.n_experts) {
-    // host side of the batched prefill's routing, for its largest chunk
-    const size_t rk = (size_t)std::max(1, std::min(kPrefillChunk, c.max_seq)) * c.top_k;
-    h->moe_ids.resize(rk);
-    h->moe_perm.resize(rk);
-    h->moe_inv.resize(rk);
-    h->moe_tiles.resize(3 * moe_max_tiles(rk, c.n_experts));
-    h->moe_off.resize(c.n_experts + 1);
-    h->moe_fill.resize(c.n_experts);
-  }
   if ((rc = scratch_setup(h->device))) return bail(rc);
   *out = h;
   g_err.clear();
@@ -490,14 +479,14 @@ int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logit
 
 // Mixture-of-experts FFN of one chunk and layer (hi/lo hold the normed
 // input): router product, routing per position, positions grouped by expert
-// on the host, the routed experts' products over their grouped rows as one
+// on the device, the routed experts' products over their grouped rows as one
 // grouped launch per product, shared experts over all rows, and the weighted
 // expert outputs summed back in rank order.
 struct MoeWs {
   float *R, *wts, *Gc, *Uc, *Yc;
   int *ids, *perm, *inv, *tiles;
   __half *ch, *cl, *sh, *sl;
-  int *h_ids, *h_perm, *h_inv, *h_tiles, *off, *fill;   // host, owned by the handle
+  int* fill;                                             // int[E]
 };
 
 // Row tiles of the grouped products: at most rows / 64 + E of them.
@@ -514,35 +503,14 @@ int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int T
   int rc;
   if ((rc = ok(kie::launch_gemm(hi, lo, d, w.router, d, m.R, E, Tn, E, d, false, s)))) return rc;
   if ((rc = ok(kie::launch_route(m.R, E, k, p.moe_renorm, m.ids, m.wts, p.expert_log, p.L, l, c0, Tn, s)))) return rc;
-  KIE_HIP(hipMemcpyAsync(m.h_ids, m.ids, sizeof(int) * rows, hipMemcpyDeviceToHost, s));
-  KIE_HIP(hipStreamSynchronize(s));
-  // compact rows ordered by expert, then position: perm[q] = t * k + a
-  std::fill(m.off, m.off + E + 1, 0);
-  for (int i = 0; i < rows; ++i) ++m.off[m.h_ids[i] + 1];
-  for (int e = 0; e < E; ++e) m.off[e + 1] += m.off[e];
-  std::copy(m.off, m.off + E, m.fill);
-  for (int i = 0; i < rows; ++i) {
-    const int q = m.fill[m.h_ids[i]]++;
-    m.h_perm[q] = i;
-    m.h_inv[i] = q;
-  }
-  // row tiles of at most 64 rows that never straddle two experts
-  int nt = 0;
-  for (int e = 0; e < E; ++e)
-    for (int r0 = m.off[e]; r0 < m.off[e + 1]; r0 += 64, ++nt) {
-      m.h_tiles[3 * nt] = r0;
-      m.h_tiles[3 * nt + 1] = std::min(r0 + 64, m.off[e + 1]);
-      m.h_tiles[3 * nt + 2] = e;
-    }
-  KIE_HIP(hipMemcpyAsync(m.perm, m.h_perm, sizeof(int) * rows, hipMemcpyHostToDevice, s));
-  KIE_HIP(hipMemcpyAsync(m.inv, m.h_inv, sizeof(int) * rows, hipMemcpyHostToDevice, s));
-  KIE_HIP(hipMemcpyAsync(m.tiles, m.h_tiles, sizeof(int) * 3 * nt, hipMemcpyHostToDevice, s));
+  const int mt = (int)moe_max_tiles((size_t)rows, E);
+  if ((rc = ok(kie::launch_moe_group(m.ids, rows, E, m.fill, m.tiles, mt, m.perm, m.inv, s)))) return rc;
   if ((rc = ok(kie::launch_gather_rows(hi, lo, d, m.perm, k, m.ch, m.cl, rows, s)))) return rc;
   const size_t gate_e = (size_t)Fe * d, down_e = (size_t)d * Fe;
-  if ((rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_gate, gate_e, d, m.Gc, Fe, m.tiles, nt, Fe, d, s))) ||
-      (rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_up, gate_e, d, m.Uc, Fe, m.tiles, nt, Fe, d, s))) ||
+  if ((rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_gate, gate_e, d, m.Gc, Fe, m.tiles, mt, Fe, d, s))) ||
+      (rc = ok(kie::launch_gemm_grouped(m.ch, m.cl, d, w.e_up, gate_e, d, m.Uc, Fe, m.tiles, mt, Fe, d, s))) ||
       (rc = ok(kie::launch_swiglu_w_split(m.Gc, m.Uc, Fe, rows, m.perm, m.wts, m.sh, m.sl, s))) ||
-      (rc = ok(kie::launch_gemm_grouped(m.sh, m.sl, Fe, w.e_down, down_e, Fe, m.Yc, d, m.tiles, nt, d, Fe, s))))
+      (rc = ok(kie::launch_gemm_grouped(m.sh, m.sl, Fe, w.e_down, down_e, Fe, m.Yc, d, m.tiles, mt, d, Fe, s))))
     return rc;
   for (int a = 0; a < p.nshared; ++a) {
     const size_t es = (size_t)(E + a);
@@ -604,6 +572,7 @@ size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
     char* perm = take(sizeof(int) * rk);
     char* inv = take(sizeof(int) * rk);
     char* tiles = take(sizeof(int) * 3 * moe_max_tiles(rk, p.E));
+    char* fill = take(sizeof(int) * p.E);
     char* ch = take(sizeof(__half) * rows_d);
     char* cl = take(sizeof(__half) * rows_d);
     char* sh = take(sizeof(__half) * rx * Fe);
@@ -619,6 +588,7 @@ size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
       m.perm = reinterpret_cast<int*>(perm);
       m.inv = reinterpret_cast<int*>(inv);
       m.tiles = reinterpret_cast<int*>(tiles);
+      m.fill = reinterpret_cast<int*>(fill);
       m.ch = reinterpret_cast<__half*>(ch);
       m.cl = reinterpret_cast<__half*>(cl);
       m.sh = reinterpret_cast<__half*>(sh);
@@ -637,14 +607,6 @@ int prefill_batched(kie_handle* h, int n, int T, char* ws) {
   PfWs W{};
   (void)prefill_ws(p, T, ws, &W);
   MoeWs& mw = W.m;
-  if (moe) {
-    mw.h_ids = h->moe_ids.data();
-    mw.h_perm = h->moe_perm.data();
-    mw.h_inv = h->moe_inv.data();
-    mw.h_tiles = h->moe_tiles.data();
-    mw.off = h->moe_off.data();
-    mw.fill = h->moe_fill.data();
-  }
   float* X = W.X;
   float* QKV = W.QKV;
   float* O = W.O;
