@@ -469,8 +469,8 @@ int kie_prefill(kie_handle* h, const int32_t* tokens, int32_t n) {
 }
 
 namespace {
-int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
-                 float temperature, uint64_t seed, int top_k = 0, float top_p = 1.f);
+static int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
+                        float temperature, uint64_t seed, int top_k = 0, float top_p = 1.f);
 
 // Batched prefill of positions 0 .. n - 2 in chunks of kPrefillChunk positions.
 // Per chunk and layer: RMSNorm -> Q/K/V products -> RoPE + fp16 K/V rows into
@@ -492,7 +492,7 @@ struct MoeWs {
 // Row tiles of the grouped products: at most rows / 64 + E of them.
 size_t moe_max_tiles(size_t rows, int E) { return rows / 64 + (size_t)E + 1; }
 
-int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int Tn, const __half* hi,
+static int moe_ffn_batched(kie_handle* h, const kie::LayerPtrs& w, int l, int c0, int Tn, const __half* hi,
                     const __half* lo, float* X, MoeWs& m) {
   const kie::Params& p = h->base;
   hipStream_t s = h->stream;
@@ -533,7 +533,7 @@ struct PfWs {
   MoeWs m;
 };
 
-size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
+static size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
   const bool moe = p.E != 0;
   const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
   const int wide = std::max(std::max(d, qd), F);
@@ -600,7 +600,7 @@ size_t prefill_ws(const kie::Params& p, int T, char* base, PfWs* w) {
 
 // Prefill of positions 0 .. n - 2 in chunks of T positions, with the
 // workspace `ws` carved for T (prefill_ws).  No allocation.
-int prefill_batched(kie_handle* h, int n, int T, char* ws) {
+static int prefill_batched(kie_handle* h, int n, int T, char* ws) {
   const kie::Params& p = h->base;
   const bool moe = p.E != 0;
   const int d = p.d, qd = p.H * p.hd, kd = p.nkv * p.hd, F = moe ? 0 : p.F, qkv = qd + 2 * kd;
@@ -656,7 +656,7 @@ int prefill_batched(kie_handle* h, int n, int T, char* ws) {
 }
 
 // Validation shared by both batched prefill entries (nothing launched).
-int prefill_batched_check(kie_handle* h, const int32_t* tokens, int32_t n) {
+static int prefill_batched_check(kie_handle* h, const int32_t* tokens, int32_t n) {
   if (!h || !tokens) return fail(KIE_ERR_INVALID_ARG, "handle or tokens is NULL");
   if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
   if (h->pos != 0 || h->pending) return fail(KIE_ERR_BAD_STATE, "prefill needs a fresh or reset handle");
@@ -674,7 +674,7 @@ int prefill_batched_check(kie_handle* h, const int32_t* tokens, int32_t n) {
 
 // Runs a validated batched prefill with chunks of T positions in workspace
 // `ws` and makes the last prompt token pending.
-int prefill_batched_run(kie_handle* h, const int32_t* tokens, int32_t n, int T, char* ws) {
+static int prefill_batched_run(kie_handle* h, const int32_t* tokens, int32_t n, int T, char* ws) {
   KIE_HIP(hipMemcpyAsync(h->d_prompt, tokens, sizeof(int) * n, hipMemcpyHostToDevice, h->stream));
   KIE_HIP(hipEventRecord(h->ev0, h->stream));
   int rc = prefill_batched(h, n, T, ws);
@@ -720,7 +720,7 @@ int scratch_setup(int dev) {
   return KIE_OK;
 }
 
-void* scratch_of(int dev) {
+static void* scratch_of(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   return g_scratch_ptr[dev];
@@ -833,7 +833,7 @@ int kie_decode_sampled_topkp(kie_handle* h, int32_t n, uint64_t seed, float temp
 }
 
 namespace {
-int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
+static int decode_steps(kie_handle* h, int32_t n, int32_t* out_tokens, float* out_logits, int sample,
                  float temperature, uint64_t seed, int top_k, float top_p) {
   if (!h) return fail(KIE_ERR_INVALID_ARG, "handle is NULL");
   if (h->broken) return fail(KIE_ERR_BAD_STATE, "handle is broken; call kie_reset");
@@ -1087,7 +1087,7 @@ constexpr int kStageMap[] = {0, 1, 3, 4, 5, 6, 7, 8, 9};
 constexpr int kNumStages = (int)(sizeof(kStageMap) / sizeof(kStageMap[0]));
 constexpr int kSlotQkv = 0, kSlotO = 2, kSlotXO = 3, kSlotRouter = 4, kSlotU = 5, kSlotXDown = 6;
 
-kie::Params debug_params(const kie_handle* h) {
+static kie::Params debug_params(const kie_handle* h) {
   kie::Params p = h->base;
   p.trace = nullptr;
   p.mode = kie::kDecode;

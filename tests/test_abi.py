@@ -1,6 +1,8 @@
 """C-ABI checks that need no GPU: libkie.so loads, exports every function
 include/kie.h declares, and validates configurations on the host."""
 import ctypes
+import shutil
+import subprocess
 
 import pytest
 
@@ -21,6 +23,18 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     missing = [n for n in _lib.declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_library_exports_nothing_else_with_c_linkage():
+    # the internal helpers of the runtime must not leak into the C namespace
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not available")
+    out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {f[2] for f in (line.split() for line in out.splitlines())
+                if len(f) == 3 and f[1] == "T" and not f[2].startswith("_Z")}
+    assert exported == set(_lib.declared_functions()), sorted(exported ^ set(_lib.declared_functions()))
 
 
 @pytest.mark.parametrize("name", sorted(PRESETS))
