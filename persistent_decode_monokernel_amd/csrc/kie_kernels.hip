@@ -1129,39 +1129,66 @@ __device__ __forceinline__ bool attn_gather_merge(const Params& p, int step, int
   return true;
 }
 
-template <int G, bool kPre, bool kMerge>
-__device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int pos, const AttnUnit& U,
-                                          float* lds, KVPre pre, const Ctl& c, Tracer& tr) {
-  const int hd = p.hd, half = hd >> 1, S = attn_splits(p, pos);
-  const int qd = p.H * hd, kd = p.nkv * hd;
-  const int g = U.g, sidx = U.sidx, p0 = U.p0, pend = U.pend;
-  const bool has_new = U.has_new;
+// The end of an attention unit, once every wave has written its online-
+// softmax state (acc, m, l per query head) to a.wst: merges the waves in
+// order and publishes this split's partial (or o itself when S == 1); the
+// merging splits then gather and merge their heads.
+template <int G, bool kMerge>
+__device__ __forceinline__ bool attn_finish(const Params& p, int step, int l, int g, int S, int sidx,
+                                            float* lds, const Ctl& c) {
+  const int hd = p.hd, ws = hd + 2;
   const AttnLds a = attn_lds<G>(p, lds);
-
-  const size_t hb = kv_head_base(p, l, g);
-  const unsigned bytes = (unsigned)((size_t)p.cap * hd * 2);
-  const Rsrc rk = make_rsrc(p.kc + hb, bytes);
-  const Rsrc rv = make_rsrc(p.vc + hb, bytes);
-
-  // first step of cache rows: prefetched before the wait, or now
-  u32x4 kr[kAU], vr[kAU];
-  if (kPre) {
-#pragma unroll
-    for (int u = 0; u < kAU; ++u) {
-      kr[u] = pre.k[u];
-      vr[u] = pre.v[u];
+  __syncthreads();
+  const unsigned fp = ll_flag(p, step, l, kSlotPart);
+  const unsigned fo = ll_flag(p, step, l, kSlotO);
+  for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
+    const int h = (2 * t) / hd, i = (2 * t) % hd;
+    float M = kNegBig;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, a.wst[(w * G + h) * ws + hd]);
+    float Ls = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float* st = a.wst + (w * G + h) * ws;
+      const float sc = exp2f(st[hd] - M);
+      Ls = fmaf(st[hd + 1], sc, Ls);
+      A0 = fmaf(st[i], sc, A0);
+      A1 = fmaf(st[i + 1], sc, A1);
     }
-  } else {
-    kv_load_step(p, rk, rv, p0, pend, kr, vr);
+    if (S == 1) {
+      ll_put2(p, p.off_o + ((g * G + h) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
+    } else {
+      ll_put(p, part_word(p, g, G, sidx, h, i), A0, fp);
+      ll_put(p, part_word(p, g, G, sidx, h, i + 1), A1, fp);
+      if (i == 0) {
+        ll_put(p, part_word(p, g, G, sidx, h, hd), M, fp);
+        ll_put(p, part_word(p, g, G, sidx, h, hd + 1), Ls, fp);
+      }
+    }
   }
+  if (kMerge && S > 1 && sidx < G) {
+    __syncthreads();
+    return attn_gather_merge<G>(p, step, l, g, S, sidx, S, lds, c);
+  }
+  return true;
+}
 
+// The start of an attention unit: gathers the raw q of the G heads (and
+// the new k, v for the split holding pos), rotates q (scaled by
+// log2(e)/sqrt(hd)) into a.qs, rounds the rotated new k and v to fp16 into
+// a.kn / a.vn and appends them to the cache.  Marks the trace after the
+// gather and at the end.
+template <int G, class Issue>
+__device__ __forceinline__ bool attn_prologue(const Params& p, int step, int l, int pos, int g, size_t hb,
+                                              bool has_new, const AttnLds& a, const Ctl& c, Tracer& tr,
+                                              Issue&& issue) {
+  const int hd = p.hd, half = hd >> 1;
+  const int qd = p.H * hd, kd = p.nkv * hd;
   // raw q of the G heads (and the new k, v for the split holding pos)
   {
     const unsigned fq = ll_flag(p, step, l, kSlotQkv);
     const LLRange rg[3] = {{p.off_qkv + g * G * hd, G * hd, a.qs, fq},
                            {p.off_qkv + qd + g * hd, has_new ? hd : 0, a.kn, fq},
                            {p.off_qkv + qd + kd + g * hd, has_new ? hd : 0, a.vn, fq}};
-    if (!ll_gather(p, rg, c)) return false;
+    if (!ll_gather(p, rg, c, issue)) return false;
   }
   mark(tr);
 
@@ -1217,6 +1244,36 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
   }
   __syncthreads();
   mark(tr);
+  return true;
+}
+
+template <int G, bool kPre, bool kMerge>
+__device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int pos, const AttnUnit& U,
+                                          float* lds, KVPre pre, const Ctl& c, Tracer& tr) {
+  const int hd = p.hd, half = hd >> 1, S = attn_splits(p, pos);
+  const int qd = p.H * hd, kd = p.nkv * hd;
+  const int g = U.g, sidx = U.sidx, p0 = U.p0, pend = U.pend;
+  const bool has_new = U.has_new;
+  const AttnLds a = attn_lds<G>(p, lds);
+
+  const size_t hb = kv_head_base(p, l, g);
+  const unsigned bytes = (unsigned)((size_t)p.cap * hd * 2);
+  const Rsrc rk = make_rsrc(p.kc + hb, bytes);
+  const Rsrc rv = make_rsrc(p.vc + hb, bytes);
+
+  // first step of cache rows: prefetched before the wait, or now
+  u32x4 kr[kAU], vr[kAU];
+  if (kPre) {
+#pragma unroll
+    for (int u = 0; u < kAU; ++u) {
+      kr[u] = pre.k[u];
+      vr[u] = pre.v[u];
+    }
+  } else {
+    kv_load_step(p, rk, rv, p0, pend, kr, vr);
+  }
+
+  if (!attn_prologue<G>(p, step, l, pos, g, hb, has_new, a, c, tr, [] {})) return false;
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int grp = lane >> 4, sub = lane & 15;
@@ -1353,38 +1410,249 @@ __device__ __forceinline__ bool attn_unit(const Params& p, int step, int l, int 
       }
     }
   }
+  return attn_finish<G, kMerge>(p, step, l, g, S, sidx, lds, c);
+}
+
+// ---- Matrix-core flash-decode unit (G >= 2 query heads per KV head, hd a
+// multiple of 16 up to 80).  With G heads sharing every cached row the vector form
+// spends most of its time on per-head dot products and lane reductions; here
+// a wave takes 32 cached positions (a tile) at a time and both products run
+// on v_mfma_f32_32x32x16_f16:
+//   scores: rows = the G query heads (zero beyond G), columns = positions,
+//           16 dimensions per step; q is split into fp16 high and low parts
+//           (K is exact in fp16), so the product is fp32 up to rounding order;
+//   output: rows = heads, columns = 32 dimensions per column tile, 16
+//           positions per step, with P split high/low and V staged transposed
+//           in the wave's own LDS tile.
+// Lane l holds position l & 31 of the tile (dimensions 16 s + 8 (l >> 5) ..
+// + 7 of step s) for the score product, and its lanes 0..31 hold the G
+// scores of one position each, so the online softmax is a reduction across
+// the wave.  Each wave keeps its own (acc, m, l) per head; attn_finish merges
+// the waves as for the vector form.
+typedef _Float16 mh8 __attribute__((ext_vector_type(8)));
+typedef float mf16 __attribute__((ext_vector_type(16)));
+constexpr int kMT = 32;                      // positions per tile
+constexpr int kMTS = kMT + 8;                // LDS row stride (halves): transposed V, P
+constexpr int kMaxNS = 5;                    // 16-wide steps of the score product: hd <= 80
+constexpr int kMaxCT = (kMaxNS + 1) / 2;     // 32-wide column tiles of the output
+// (a wider head keeps the vector form: its K/V fragments and accumulators
+// would not fit the register budget)
+
+__device__ __forceinline__ int mfma_cols(int hd) { return 32 * ((hd / 16 + 1) / 2); }
+
+struct MfmaPre {
+  u32x4 k[kMaxNS];
+};
+
+// Above the wave states (and over the merging split's partial buffer, which
+// is used only once the tiles are done): q high/low [G][hd], each wave's
+// transposed V tile [cols][kMTS] and P high/low [G][kMTS] (halves).
+struct MfmaLds {
+  _Float16 *qh, *ql, *vt, *ph, *pl;
+};
+template <int G>
+__device__ __forceinline__ MfmaLds mfma_lds(const Params& p, const AttnLds& a) {
+  const int hd = p.hd;
+  const int base = (kWaves * G * (p.hd + 2) + 3) & ~3;        // floats past a.wst, 16-byte aligned
+  MfmaLds m;
+  m.qh = reinterpret_cast<_Float16*>(a.wst + base);
+  m.ql = m.qh + G * hd;
+  m.vt = m.ql + G * hd;
+  m.ph = m.vt + kWaves * mfma_cols(hd) * kMTS;
+  m.pl = m.ph + kWaves * G * kMTS;
+  return m;
+}
+
+// The LDS writes of the calling wave are complete and visible to all its
+// lanes (a wave-scope release/acquire around the wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// K (or V) rows of the tile starting at position kbase in the score
+// product's layout; positions at or past pend read zeros.
+__device__ __forceinline__ void mfma_rows_load(const Params& p, Rsrc r, int kbase, int pend,
+                                               u32x4 (&k)[kMaxNS]) {
+  const int lane = threadIdx.x & 63;
+  const int j = kbase + (lane & 31), kin = 8 * (lane >> 5), NS = p.hd >> 4;
+  const unsigned row = (unsigned)j * (unsigned)p.hd * 2u;
+#pragma unroll
+  for (int s = 0; s < kMaxNS; ++s)
+    k[s] = ld_kv16(r, (s < NS && j < pend) ? row + (unsigned)(16 * s + kin) * 2u : kOffNone);
+}
+
+__device__ __forceinline__ u32x4 pack_h8(const float* f) {
+  mh8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)f[i];
+  return __builtin_bit_cast(u32x4, h);
+}
+
+template <int G, bool kPre, bool kMerge>
+__device__ __forceinline__ bool attn_unit_mfma(const Params& p, int step, int l, int pos, const AttnUnit& U,
+                                               float* lds, const MfmaPre& pre, const Ctl& c, Tracer& tr) {
+  const int hd = p.hd, S = attn_splits(p, pos), NS = hd >> 4, NCT = (NS + 1) >> 1, cols = mfma_cols(hd);
+  const int g = U.g, sidx = U.sidx, p0 = U.p0, pend = U.pend;
+  const bool has_new = U.has_new;
+  const int kend = has_new ? pos + 1 : pend;          // this unit's positions: [p0, kend)
+  const AttnLds a = attn_lds<G>(p, lds);
+  const MfmaLds ml = mfma_lds<G>(p, a);
+  const size_t hb = kv_head_base(p, l, g);
+  const unsigned bytes = (unsigned)((size_t)p.cap * hd * 2);
+  const Rsrc rk = make_rsrc(p.kc + hb, bytes);
+  const Rsrc rv = make_rsrc(p.vc + hb, bytes);
+  const int lane = threadIdx.x & 63, wave = wave_id(), l32 = lane & 31, kin = 8 * (lane >> 5);
+
+  // K of the wave's first tile: prefetched before the wait, or now
+  u32x4 kt[kMaxNS], vt[kMaxNS];
+  if (kPre) {
+#pragma unroll
+    for (int s = 0; s < kMaxNS; ++s) kt[s] = pre.k[s];
+  } else {
+    mfma_rows_load(p, rk, p0 + kMT * wave, pend, kt);
+  }
+  // (V is loaded per tile once q has arrived: loads in flight during the
+  // wait delay the polls behind them)
+  if (!attn_prologue<G>(p, step, l, pos, g, hb, has_new, a, c, tr, [] {})) return false;
+
+  // q as fp16 high and low parts; the padded columns of this wave's V tile
+  for (int i = threadIdx.x; i < G * hd; i += kThreads) {
+    const float v = a.qs[i];
+    const _Float16 hi = (_Float16)v;
+    ml.qh[i] = hi;
+    ml.ql[i] = (_Float16)(v - (float)hi);
+  }
+  _Float16* vtw = ml.vt + wave * cols * kMTS;
+  _Float16* phw = ml.ph + wave * G * kMTS;
+  _Float16* plw = ml.pl + wave * G * kMTS;
+  for (int e = lane; e < (cols - hd) * kMTS; e += 64) vtw[hd * kMTS + e] = (_Float16)0.f;
   __syncthreads();
-  // merge the waves in order: this split's partial (or o itself when S == 1)
-  const unsigned fp = ll_flag(p, step, l, kSlotPart);
-  const unsigned fo = ll_flag(p, step, l, kSlotO);
-  for (int t = threadIdx.x; 2 * t < G * hd; t += kThreads) {      // elements i, i + 1 of head h
-    const int h = (2 * t) / hd, i = (2 * t) % hd;
-    float M = kNegBig;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, a.wst[(w * G + h) * ws + hd]);
-    float Ls = 0.f, A0 = 0.f, A1 = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float* st = a.wst + (w * G + h) * ws;
-      const float sc = exp2f(st[hd] - M);
-      Ls = fmaf(st[hd + 1], sc, Ls);
-      A0 = fmaf(st[i], sc, A0);
-      A1 = fmaf(st[i + 1], sc, A1);
+
+  float m[G], ls[G];
+  mf16 acc[kMaxCT];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    ls[h] = 0.f;
+  }
+#pragma unroll
+  for (int ct = 0; ct < kMaxCT; ++ct) acc[ct] = (mf16){};
+  const int ntiles = (kend - p0 + kMT - 1) / kMT;
+  // per-lane LDS bases; every access below adds a constant offset
+  const int qrow = l32 < G ? l32 : 0;                 // lanes past the heads read a valid row, then zero it
+  const _Float16* qhr = ml.qh + qrow * hd + kin;      // q fragments
+  const _Float16* qlr = ml.ql + qrow * hd + kin;
+  _Float16* vw = vtw + kin * kMTS + l32;              // V transpose: this lane's position column
+  const _Float16* vr = vtw + l32 * kMTS + kin;        // V fragments: dimension row l32 (+ 32 ct)
+  _Float16* pwh = phw + l32;                          // P of this lane's position
+  _Float16* pwl = plw + l32;
+  const _Float16* prh = phw + qrow * kMTS + kin;      // P fragments: head row
+  const _Float16* prl = plw + qrow * kMTS + kin;
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int kbase = p0 + kMT * t;
+    if (t != wave) mfma_rows_load(p, rk, kbase, pend, kt);
+    mfma_rows_load(p, rv, kbase, pend, vt);
+    const int j = kbase + l32;
+    const bool is_new = has_new && j == pos;            // the new position: its rounded rows from LDS
+    if (is_new) {
+#pragma unroll
+      for (int s = 0; s < kMaxNS; ++s)
+        if (s < NS) kt[s] = pack_h8(a.kn + 16 * s + kin);
     }
-    if (S == 1) {
-      ll_put2(p, p.off_o + ((g * G + h) * hd + i) / 2, A0 / Ls, A1 / Ls, fo);
-    } else {
-      ll_put(p, part_word(p, g, G, sidx, h, i), A0, fp);
-      ll_put(p, part_word(p, g, G, sidx, h, i + 1), A1, fp);
-      if (i == 0) {
-        ll_put(p, part_word(p, g, G, sidx, h, hd), M, fp);
-        ll_put(p, part_word(p, g, G, sidx, h, hd + 1), Ls, fp);
+    // scores of the G heads against the tile's positions
+    mf16 sa = (mf16){};
+#pragma unroll
+    for (int s = 0; s < kMaxNS; ++s) {
+      if (s < NS) {
+        mh8 ah = *reinterpret_cast<const mh8*>(qhr + 16 * s);
+        mh8 al = *reinterpret_cast<const mh8*>(qlr + 16 * s);
+        if (l32 >= G) {
+          ah = (mh8){};
+          al = (mh8){};
+        }
+        const mh8 b = __builtin_bit_cast(mh8, kt[s]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, b, sa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, sa, 0, 0, 0);
+      }
+    }
+    // online softmax: lanes 0..31 hold position j's score of head h in sa[h]
+    const bool valid = lane < 32 && j < kend;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sc = valid ? sa[h] : kNegBig;
+      const float mn = fmaxf(m[h], wave_max(sc));
+      const float corr = exp2f(m[h] - mn);
+      const float pw = valid ? exp2f(sc - mn) : 0.f;
+      ls[h] = ls[h] * corr + wave_sum(pw);
+      m[h] = mn;
+#pragma unroll
+      for (int ct = 0; ct < kMaxCT; ++ct) acc[ct][h] *= corr;
+      if (lane < 32) {
+        const _Float16 hi = (_Float16)pw;
+        pwh[h * kMTS] = hi;
+        pwl[h * kMTS] = (_Float16)(pw - (float)hi);
+      }
+    }
+    // V into the wave's LDS tile, transposed: [dimension][position]
+    if (is_new) {
+#pragma unroll
+      for (int s = 0; s < kMaxNS; ++s)
+        if (s < NS) vt[s] = pack_h8(a.vn + 16 * s + kin);
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxNS; ++s) {
+      if (s < NS) {
+        const mh8 vh = __builtin_bit_cast(mh8, vt[s]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vw[(16 * s + i) * kMTS] = vh[i];
+      }
+    }
+    wave_sync();                                       // the V tile and P are the wave's own
+#pragma unroll
+    for (int kk = 0; kk < kMT; kk += 16) {
+      mh8 ah = *reinterpret_cast<const mh8*>(prh + kk);
+      mh8 al = *reinterpret_cast<const mh8*>(prl + kk);
+      if (l32 >= G) {
+        ah = (mh8){};
+        al = (mh8){};
+      }
+#pragma unroll
+      for (int ct = 0; ct < kMaxCT; ++ct) {
+        if (ct < NCT) {
+          const mh8 b = *reinterpret_cast<const mh8*>(vr + 32 * ct * kMTS + kk);
+          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, b, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, acc[ct], 0, 0, 0);
+        }
+      }
+    }
+    wave_sync();                                       // reads done before the next tile's writes
+  }
+  // the wave's state: lanes 0..31 hold dimension 32 ct + l32 of head h in acc[ct][h]
+  const int ws = hd + 2;
+  if (lane < 32) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* st = a.wst + (wave * G + h) * ws;
+#pragma unroll
+      for (int ct = 0; ct < kMaxCT; ++ct) {
+        const int d = 32 * ct + l32;
+        if (ct < NCT && d < hd) st[d] = acc[ct][h];
+      }
+      if (lane == 0) {
+        st[hd] = m[h];
+        st[hd + 1] = ls[h];
       }
     }
   }
-  if (kMerge && S > 1 && sidx < G) {
-    __syncthreads();
-    return attn_gather_merge<G>(p, step, l, g, S, sidx, S, lds, c);
-  }
-  return true;
+  return attn_finish<G, kMerge>(p, step, l, g, S, sidx, lds, c);
 }
 
 // Units wg, wg + n_wg, ... of this workgroup (one unit unless the grid is
@@ -1398,6 +1666,25 @@ __device__ __forceinline__ bool stage_attn(const Params& p, int step, int l, int
     mark(tr);
     mark(tr);
     return true;
+  }
+  if constexpr (G >= 2) {
+    if ((p.hd & 15) == 0 && p.hd <= 16 * kMaxNS) {
+      const AttnUnit u0 = attn_unit_of(p, pos, wg);
+      const size_t hb = kv_head_base(p, l, u0.g);
+      const unsigned bytes = (unsigned)((size_t)p.cap * p.hd * 2);
+      MfmaPre mp;
+      mfma_rows_load(p, make_rsrc(p.kc + hb, bytes), u0.p0 + kMT * wave_id(), u0.pend, mp.k);
+      if (!attn_unit_mfma<G, true, kMerge>(p, step, l, pos, u0, s.h, mp, c, tr)) return false;
+      __syncthreads();
+      for (int u = wg + p.n_wg; u < units; u += p.n_wg) {
+        Tracer none{nullptr, 0};
+        if (!attn_unit_mfma<G, false, kMerge>(p, step, l, pos, attn_unit_of(p, pos, u), s.h, MfmaPre{}, c,
+                                              none))
+          return false;
+        __syncthreads();
+      }
+      return true;
+    }
   }
   const KVPre pre = prefetch_attn(p, l, pos, wg);
   if (!attn_unit<G, true, kMerge>(p, step, l, pos, attn_unit_of(p, pos, wg), s.h, pre, c, tr))

@@ -168,6 +168,15 @@ __host__ __device__ inline LdsLayout lds_layout(const Params& p) {
   const int S = p.splits > 1 ? p.splits : 1;
   const int attn = gpad * p.hd + 2 * p.hd + (kWaves + S) * gpad * (p.hd + 2);
   v = v > attn ? v : attn;
+  if (G >= 2 && p.hd % 16 == 0 && p.hd <= 80) {
+    // the matrix-core attention unit: q high/low, and per wave a transposed
+    // V tile (32 positions x the head dimension rounded up to 32) and P
+    // high/low, all fp16, above the wave states
+    const int cols = 32 * ((p.hd / 16 + 1) / 2);
+    const int halves = 2 * gpad * p.hd + kWaves * cols * 40 + 2 * kWaves * gpad * 40;
+    const int mm = gpad * p.hd + 2 * p.hd + ((kWaves * gpad * (p.hd + 2) + 3) & ~3) + (halves + 1) / 2;
+    v = v > mm ? v : mm;
+  }
   LdsLayout L;
   L.hcap = (v + 63) & ~63;
   L.part_off = L.hcap;
