@@ -23,9 +23,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# the files that define the decode kernel's code and parameter layout (the
+# host runtime only launches it)
 KERNEL_SOURCES = ("persistent_decode_monokernel_amd/csrc/kie_kernels.hip",
-                  "persistent_decode_monokernel_amd/csrc/kie_params.h",
-                  "persistent_decode_monokernel_amd/csrc/kie_runtime.hip")
+                  "persistent_decode_monokernel_amd/csrc/kie_params.h")
 # HBM bytes of one timed decode launch, from two rocprofv3 counter passes
 # (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for the
 # streaming probe kernel of known size; the summary with the commands is

