@@ -377,6 +377,44 @@ def test_variant_decode_parity(torch, kie, key):
     eng.close()
 
 
+# Grouped-query attention shapes: the matrix-core form (head size a multiple
+# of 16 up to 80) at several head sizes and group sizes, a small grid (so a
+# split holds several 32-position tiles per wave, or a workgroup runs several
+# units), and the vector form that a wider head keeps.
+GQA_SHAPES = {
+    "g2_hd16": dict(n_heads=8, n_kv_heads=4, head_dim=16, n_workgroups=0, prompt_len=90),
+    "g4_hd48": dict(n_heads=8, n_kv_heads=2, head_dim=48, n_workgroups=0, prompt_len=90),
+    "g2_hd64_tiles": dict(n_heads=4, n_kv_heads=2, head_dim=64, n_workgroups=4, prompt_len=700),
+    "g4_hd80_units": dict(n_heads=16, n_kv_heads=4, head_dim=80, n_workgroups=3, prompt_len=150),
+    "g2_hd128_vector": dict(n_heads=4, n_kv_heads=2, head_dim=128, n_workgroups=64, prompt_len=90),
+}
+
+
+@pytest.mark.parametrize("key", sorted(GQA_SHAPES))
+def test_grouped_attention_shapes(torch, kie, key):
+    kw = dict(GQA_SHAPES[key])
+    nwg = kw.pop("n_workgroups")
+    cfg = _model("tiny", n_layers=2, n_decode=24, **kw)
+    _say("grouped attention", key)
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    n = cfg.n_decode
+    extra = {"n_workgroups": nwg} if nwg else {}
+    eng, toks, z = _run_gpu(torch, kie, cfg, W, prompt, n, **extra)
+    o, zo = _oracle_replay(cfg, weights_to_numpy(W), prompt, toks)
+    rep = compare_steps(z, toks, zo)
+    _say(key, rep)
+    assert rep["pinned"] >= n // 4
+    P = len(prompt)
+    _check_kv(eng, o, (0, 1), [(0, 8), (P - 40, P - 1 + n)])
+    eng.close()
+    # the staged mode runs the same units one stage per kernel: same bits
+    eg, tg, zg = _run_gpu(torch, kie, cfg, W, prompt, n, graph=True, **extra)
+    np.testing.assert_array_equal(tg, toks)
+    np.testing.assert_array_equal(zg, z)
+    eg.close()
+
+
 def test_gqa_merge_with_fewer_splits_than_heads(torch, kie):
     """Grouped-query attention (4 query heads per KV head) at positions
     199..298, where the context-sized split count is 2, then 3: fewer splits
