@@ -213,23 +213,11 @@ struct GridSync {
   unsigned grp;
   long long ticks;
   int spin_limit;
-  unsigned long long* tr;   // this workgroup's trace slots while a step is traced, else null
-  int ev;                   // next trace slot
 };
-
-// Records the wall clock into the next trace slot (thread 0, traced steps only).
-__device__ __forceinline__ void trace_mark(GridSync& g) {
-  if (g.tr != nullptr) {
-    if (threadIdx.x == 0 && g.ev < kTraceEvents) g.tr[g.ev] = wall_clock64();
-    ++g.ev;
-  }
-}
 
 __device__ __forceinline__ GridSync make_sync(unsigned* ctr, int* err, unsigned n, long long ticks,
                                               int spin_limit) {
   GridSync g;
-  g.tr = nullptr;
-  g.ev = 0;
   g.ctr = ctr;
   g.err = err;
   g.epoch = 0u;
@@ -1879,32 +1867,42 @@ __device__ __forceinline__ bool stage_router(const Params& p, int step, int l, i
 // the shared experts with weight 1).
 // The maximum and the softmax denominator are wave reductions (lane i takes
 // logits i, i + 64, ...), the same in every wave of every workgroup, so all
-// workgroups agree on the routing bit for bit.  A serial loop over the
-// logits in every thread is a chain of dependent LDS reads: with 64 experts
-// it held the expert GEMV back by ~9 us per layer, against ~2.5 us now with
-// the RMSNorm included.  Ranks compare against all logits with the reads
-// unrolled.
-__device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wts, const float* rl) {
+// workgroups agree on the routing bit for bit.  The rank of logit e (how many
+// logits are larger, or equal with a lower index) is counted by all the
+// workgroup's threads, each comparing e with a slice of the others, and the
+// partial counts are added with LDS integer atomics into `cnt` (int[E]
+// scratch), so the ranks are exact whatever the order.  One wave comparing
+// every pair took ~2 us per layer with 64 experts.
+__device__ __forceinline__ void moe_routing(const Params& p, int* ids, float* wts, const float* rl,
+                                            int* cnt) {
   const int E = p.E, K = p.topk;
   const int lane = threadIdx.x & 63;
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
   float mx = kNegBig;
   for (int e = lane; e < E; e += 64) mx = fmaxf(mx, rl[e]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  mx = wave_max(mx);
   float den = 0.f;
   for (int e = lane; e < E; e += 64) den += __expf(rl[e] - mx);
   den = wave_sum(den);
-  for (int e = threadIdx.x; e < E; e += kThreads) {
+  __syncthreads();
+  const int nch = E >= kThreads ? 1 : kThreads / E;      // slices of the compared logits
+  const int jlen = (E + nch - 1) / nch;
+  for (int t = threadIdx.x; t < E * nch; t += kThreads) {
+    const int e = t % E, j0 = (t / E) * jlen, j1 = min(E, j0 + jlen);
     const float re = rl[e];
-    int rank = 0;
-#pragma unroll 16
-    for (int j = 0; j < E; ++j) {
+    int r = 0;
+    for (int j = j0; j < j1; ++j) {
       const float rj = rl[j];
-      rank += (rj > re) || (rj == re && j < e);
+      r += (rj > re) || (rj == re && j < e);
     }
+    if (r) atomicAdd(&cnt[e], r);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int rank = cnt[e];
     if (rank < K) {
       ids[rank] = e;
-      wts[rank] = __expf(re - mx) / den;
+      wts[rank] = __expf(rl[e] - mx) / den;
     }
   }
   for (int a = threadIdx.x; a < p.nshared; a += kThreads) {
@@ -1973,7 +1971,7 @@ __device__ __forceinline__ bool stage_moe_gateup(const Params& p, int step, int 
   __syncthreads();
   const LLRange rl[1] = {{p.off_router, p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
   if (!ll_gather(p, rl, c)) return false;
-  moe_routing(p, ids, wts, s.sums);
+  moe_routing(p, ids, wts, s.sums, reinterpret_cast<int*>(s.part));
   if (wg == 0 && threadIdx.x < K)
     p.expert_log[((size_t)(p.pos0 + step) * p.L + l) * K + threadIdx.x] = ids[threadIdx.x];
   const MoePairAddr addr{uniform_addr(w.e_gate), uniform_addr(w.e_up), ids, ne, Fe, p.d};
@@ -2014,7 +2012,7 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
   if (!ok) return false;
   mark(tr);
   if (!have_routing) {
-    moe_routing(p, moe_ids(s), moe_wts(s), s.sums);
+    moe_routing(p, moe_ids(s), moe_wts(s), s.sums, reinterpret_cast<int*>(s.part));
     int t0, t1;
     wave_tasks(g, g.r0, t0, t1);
     pre.a = wload(moe_down_addr(p, l, s), g, g.r0, t0, t1);
