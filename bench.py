@@ -33,16 +33,16 @@ KERNEL_SOURCES = ("persistent_decode_monokernel_amd/csrc/kie_kernels.hip",
 # profiles/mono_kernel_2b_decode512.md and profiles/mono_kernel_other_workloads.md.  A figure is reported only while the
 # kernel sources still hash to the digest it was measured on.
 MEASURED_TRAFFIC = [
-    {"sources_sha256": "3a7bc1c60502ffbb9486449366ed98e0e47c5dd94f9387441e6e552642cf6098",
-     "config": "2b", "pos0": 511, "steps": 20, "bytes": 86062994022},
-    {"sources_sha256": "3a7bc1c60502ffbb9486449366ed98e0e47c5dd94f9387441e6e552642cf6098",
-     "config": "2b", "pos0": 511, "steps": 512, "bytes": 2237176828006},
-    {"sources_sha256": "3a7bc1c60502ffbb9486449366ed98e0e47c5dd94f9387441e6e552642cf6098",
-     "config": "moe", "pos0": 511, "steps": 512, "bytes": 2282002370176},
-    {"sources_sha256": "3a7bc1c60502ffbb9486449366ed98e0e47c5dd94f9387441e6e552642cf6098",
-     "config": "longctx", "pos0": 8191, "steps": 256, "bytes": 1097625133856},
-    {"sources_sha256": "3a7bc1c60502ffbb9486449366ed98e0e47c5dd94f9387441e6e552642cf6098",
-     "config": "tp8share", "pos0": 255, "steps": 1024, "bytes": 603792897440},
+    {"sources_sha256": "f12c183ff088f3a93a09fdc7f87ceadc957c2e1ca42ebf57e44258ffa28ecbc6",
+     "config": "2b", "pos0": 511, "steps": 20, "bytes": 86062273056},
+    {"sources_sha256": "f12c183ff088f3a93a09fdc7f87ceadc957c2e1ca42ebf57e44258ffa28ecbc6",
+     "config": "2b", "pos0": 511, "steps": 512, "bytes": 2237164008736},
+    {"sources_sha256": "f12c183ff088f3a93a09fdc7f87ceadc957c2e1ca42ebf57e44258ffa28ecbc6",
+     "config": "moe", "pos0": 511, "steps": 512, "bytes": 2281995862176},
+    {"sources_sha256": "f12c183ff088f3a93a09fdc7f87ceadc957c2e1ca42ebf57e44258ffa28ecbc6",
+     "config": "longctx", "pos0": 8191, "steps": 256, "bytes": 1097725430816},
+    {"sources_sha256": "f12c183ff088f3a93a09fdc7f87ceadc957c2e1ca42ebf57e44258ffa28ecbc6",
+     "config": "tp8share", "pos0": 255, "steps": 1024, "bytes": 603567532736},
 ]
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs ~8 TB/s peak, ~2.2B fp16"
 
