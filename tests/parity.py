@@ -88,13 +88,17 @@ def kv_close(k_gpu_f16: np.ndarray, k_or: np.ndarray, what: str, ulps: float = 0
                            f"{float(np.max(np.abs(g - o))):.3e}")
 
 
-def kv_rows_close(k_gpu_f16: np.ndarray, k_or: np.ndarray, what: str, rel: float = 1e-2):
+KV_ROW_REL = 6e-3
+
+
+def kv_rows_close(k_gpu_f16: np.ndarray, k_or: np.ndarray, what: str, rel: float = KV_ROW_REL):
     """Cache rows of any layer against the oracle's fp32 rows, per (head,
     position) row: max |difference| at most ``rel`` times the row's largest
     magnitude.  Deeper layers inherit the fp16 rounding of every earlier
-    layer's cache, so they get the same relative bar as the logits; a row
-    stored at the wrong position or rotated by the wrong angle misses it by
-    orders of magnitude."""
+    layer's cache (measured at most 3.5e-3 of the row maximum over the 25
+    layers of the 2b shape, 2.6e-3 on the TP-8 share); a row stored at the
+    wrong position or rotated by the wrong angle misses the bar by orders of
+    magnitude."""
     g = k_gpu_f16.astype(np.float64)
     o = k_or.astype(np.float64)
     err = np.max(np.abs(g - o), axis=-1)
