@@ -464,6 +464,9 @@ def test_longctx_8192_prompt_attention(torch, kie):
 @pytest.mark.parametrize("name,prompt_len,n,layers", [
     ("tp8share", 256, 8, (0, 12, 24)),
     ("longctx", 256, 6, (0, 12, 24)),
+    # all 25 layers over a 2048-token prompt: splits of ~120 positions, several
+    # 32-position tiles of the matrix-core attention per split
+    ("longctx", 2048, 6, (0, 12, 24)),
     ("moe", 8, 4, (0, 11, 23)),
 ])
 def test_full_size_variant_parity_sampled(torch, kie, name, prompt_len, n, layers):
