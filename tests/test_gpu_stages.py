@@ -114,12 +114,17 @@ def _check_attention(eng, cfg, layer, pos, qkv, o):
     close(o, want.reshape(-1), scale.reshape(-1) + np.abs(want.reshape(-1)), rel=4e-5, what="attention")
 
 
-@pytest.mark.parametrize("prompt_len", [600, 40])
-def test_dense_stages_match_float64(torch, kie, prompt_len):
+@pytest.mark.parametrize("prompt_len,shape", [
+    (600, {}), (40, {}),
+    # grouped query heads (4 per KV head): the matrix-core attention
+    (600, dict(n_heads=8, n_kv_heads=2, head_dim=32)),
+    (300, dict(n_heads=16, n_kv_heads=4, head_dim=80)),
+], ids=["mha600", "mha40", "gqa4_hd32", "gqa4_hd80"])
+def test_dense_stages_match_float64(torch, kie, prompt_len, shape):
     """tiny widths; at position 599 the attention runs 5 splits and a merge,
-    at position 39 one split."""
-    cfg = get_config("tiny")
-    _say("stages dense", prompt_len)
+    at position 39 one split; the grouped shapes take the matrix-core form."""
+    cfg = get_config("tiny", **shape)
+    _say("stages dense", prompt_len, shape)
     W = _random_gains(torch, make_weights(cfg, seed=5, device="cuda"), 9)
     Wn = weights_to_numpy(W)
     prompt = make_prompt(cfg, seed=2, length=prompt_len)
