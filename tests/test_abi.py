@@ -137,6 +137,18 @@ def test_batched_prefill_and_gemm_validate_arguments_on_the_host():
         assert "2 GiB" in lib.kie_last_error().decode()
 
 
+def test_stream_probe_validates_its_shape_on_the_host():
+    # the depth, the load kind and the buffer-load size limit are checked
+    # before any pointer is looked at
+    lib = _lib.load()
+    ms = ctypes.c_float()
+    for depth, kind, nbytes, text in ((3, 0, 1024, "depth"), (16, 3, 1024, "kind"),
+                                      (8, 2, 1 << 32, "4 GiB"), (8, 0, 1000, "multiple of 16")):
+        assert lib.kie_debug_stream_ex(None, None, nbytes, 0, depth, kind, 1, ctypes.byref(ms),
+                                       None) == -1, (depth, kind, nbytes)
+        assert text in lib.kie_last_error().decode(), lib.kie_last_error()
+
+
 def test_moe_renorm_flag_is_accepted():
     rc, msg = _with(PRESETS["moe"], flags=0x10)
     assert rc == 0, msg
