@@ -188,8 +188,9 @@ class Engine:
         return ids
 
     def read_trace(self) -> np.ndarray:
-        """Barrier clock stamps of the traced step: uint64 [n_workgroups, n_events]
-        (event 0 = step start, then arrive/leave per grid barrier)."""
+        """Clock stamps (100 MHz) of the traced step: uint64 [n_workgroups, n_events];
+        event 0 is the step start, then three per stage in execution order
+        (inputs complete, main loop start, end)."""
         n_wg = 4096
         buf = np.zeros((n_wg, 1024), np.uint64)
         ne = ctypes.c_int32()

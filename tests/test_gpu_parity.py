@@ -188,6 +188,28 @@ def test_tiny_determinism_and_composability(torch, kie):
     eng.close()
 
 
+@pytest.mark.parametrize("name", ["tiny", "moe_narrow"])
+def test_trace_layout_and_results_unchanged(torch, kie, name):
+    """KIE_TRACE records, for one decode step, each workgroup's clock at the
+    step start and three times per stage (5 stages per dense layer, 6 per MoE
+    layer, then lm_head); every workgroup's stamps are in order, and tracing
+    leaves the tokens and logits bit for bit as they are."""
+    cfg = _model("tiny") if name == "tiny" else _variant("moe_narrow")
+    _say("trace", name)
+    W = _gpu_weights(torch, cfg)
+    prompt = make_prompt(cfg)
+    _, t0, z0 = _run_gpu(torch, kie, cfg, W, prompt, 8)
+    eng, t1, z1 = _run_gpu(torch, kie, cfg, W, prompt, 8, trace=True)
+    np.testing.assert_array_equal(t1, t0)
+    np.testing.assert_array_equal(z1, z0)
+    tr = eng.read_trace().astype(np.int64)
+    per_layer = 6 if cfg.is_moe else 5
+    assert tr.shape[0] > 0 and tr.shape[1] == 1 + 3 * (cfg.n_layers * per_layer + 1), tr.shape
+    assert np.all(tr[:, 0] > 0)
+    assert np.all(np.diff(tr, axis=1) >= 0)
+    eng.close()
+
+
 def test_tiny_edge_cases(torch, kie):
     cfg = _model("tiny")
     _say("tiny edges")
