@@ -410,9 +410,19 @@ __device__ __forceinline__ void gemv_block(const GemvWork& g, const Addr& addr, 
     if (t + 3 * kBatch < t1) B = wload(addr, g, b0, t + 3 * kBatch, t1);
   }
   __syncthreads();
+  // row sums over the slices in order, four loads issued ahead of the adds
   for (int i = threadIdx.x; i < nrows; i += kThreads) {
+    const float* pr = part + i * g.ks;
     float v = 0.f;
-    for (int s = 0; s < g.ks; ++s) v += part[i * g.ks + s];
+    int s = 0;
+    for (; s + 4 <= g.ks; s += 4) {
+      const float a0 = pr[s], a1 = pr[s + 1], a2 = pr[s + 2], a3 = pr[s + 3];
+      v += a0;
+      v += a1;
+      v += a2;
+      v += a3;
+    }
+    for (; s < g.ks; ++s) v += pr[s];
     sums[i] = v;
   }
   __syncthreads();
@@ -1080,10 +1090,34 @@ __device__ __forceinline__ void attn_merge(const Params& p, int step, int l, int
   for (int t = threadIdx.x; 2 * t < nh * hd; t += kThreads) {     // elements i, i + 1 of head j
     const int j = (2 * t) / hd, i = (2 * t) % hd;
     const float* hp = parts + j * S * ws;
+    // split order throughout; loads are issued ahead of the dependent
+    // max / multiply-add chains (four, then two splits at a time)
     float M = kNegBig;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, hp[s * ws + hd]);
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      const float m0 = hp[s * ws + hd], m1 = hp[(s + 1) * ws + hd];
+      const float m2 = hp[(s + 2) * ws + hd], m3 = hp[(s + 3) * ws + hd];
+      M = fmaxf(M, m0);
+      M = fmaxf(M, m1);
+      M = fmaxf(M, m2);
+      M = fmaxf(M, m3);
+    }
+    for (; s < S; ++s) M = fmaxf(M, hp[s * ws + hd]);
     float Ls = 0.f, A0 = 0.f, A1 = 0.f;
-    for (int s = 0; s < S; ++s) {
+    for (s = 0; s + 2 <= S; s += 2) {
+      const float* st = hp + s * ws;
+      const float* su = st + ws;
+      const float m0 = st[hd], l0 = st[hd + 1], x0 = st[i], y0 = st[i + 1];
+      const float m1 = su[hd], l1 = su[hd + 1], x1 = su[i], y1 = su[i + 1];
+      const float sc0 = exp2f(m0 - M), sc1 = exp2f(m1 - M);
+      Ls = fmaf(l0, sc0, Ls);
+      A0 = fmaf(x0, sc0, A0);
+      A1 = fmaf(y0, sc0, A1);
+      Ls = fmaf(l1, sc1, Ls);
+      A0 = fmaf(x1, sc1, A0);
+      A1 = fmaf(y1, sc1, A1);
+    }
+    for (; s < S; ++s) {
       const float* st = hp + s * ws;
       const float sc = exp2f(st[hd] - M);
       Ls = fmaf(st[hd + 1], sc, Ls);
