@@ -33,16 +33,16 @@ KERNEL_SOURCES = ("persistent_decode_monokernel_amd/csrc/kie_kernels.hip",
 # profiles/mono_kernel_2b_decode512.md and profiles/mono_kernel_other_workloads.md.  A figure is reported only while the
 # kernel sources still hash to the digest it was measured on.
 MEASURED_TRAFFIC = [
-    {"sources_sha256": "4b53deb9aca337560b379aed3f0ffc4331933d541f637d380788631139df59c1",
-     "config": "2b", "pos0": 511, "steps": 20, "bytes": 86058721217},
-    {"sources_sha256": "4b53deb9aca337560b379aed3f0ffc4331933d541f637d380788631139df59c1",
-     "config": "2b", "pos0": 511, "steps": 512, "bytes": 2237024220743},
-    {"sources_sha256": "4b53deb9aca337560b379aed3f0ffc4331933d541f637d380788631139df59c1",
-     "config": "moe", "pos0": 511, "steps": 512, "bytes": 2281859545695},
-    {"sources_sha256": "4b53deb9aca337560b379aed3f0ffc4331933d541f637d380788631139df59c1",
-     "config": "longctx", "pos0": 8191, "steps": 256, "bytes": 1103045485060},
-    {"sources_sha256": "4b53deb9aca337560b379aed3f0ffc4331933d541f637d380788631139df59c1",
-     "config": "tp8share", "pos0": 255, "steps": 1024, "bytes": 603619233729},
+    {"sources_sha256": "43c81171fe037f4467226a6d49c0aa49b760716d55e0cf3647b0a0cfd173f0c4",
+     "config": "2b", "pos0": 511, "steps": 20, "bytes": 86076204333},
+    {"sources_sha256": "43c81171fe037f4467226a6d49c0aa49b760716d55e0cf3647b0a0cfd173f0c4",
+     "config": "2b", "pos0": 511, "steps": 512, "bytes": 2237463797735},
+    {"sources_sha256": "43c81171fe037f4467226a6d49c0aa49b760716d55e0cf3647b0a0cfd173f0c4",
+     "config": "moe", "pos0": 511, "steps": 512, "bytes": 2281990157948},
+    {"sources_sha256": "43c81171fe037f4467226a6d49c0aa49b760716d55e0cf3647b0a0cfd173f0c4",
+     "config": "longctx", "pos0": 8191, "steps": 256, "bytes": 1099092117858},
+    {"sources_sha256": "43c81171fe037f4467226a6d49c0aa49b760716d55e0cf3647b0a0cfd173f0c4",
+     "config": "tp8share", "pos0": 255, "steps": 1024, "bytes": 603925445032},
 ]
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs ~8 TB/s peak, ~2.2B fp16"
 

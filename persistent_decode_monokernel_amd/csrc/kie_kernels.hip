@@ -560,25 +560,26 @@ __device__ __forceinline__ bool wg_all(bool ok, int* flag) {
   return *flag != 0;
 }
 
-constexpr int kGatherPer = 8;    // words per thread per pass
+constexpr int kGatherPer = 8;    // words per thread per pass (the default width)
 
-// One thread's share of a gather pass: up to kGatherPer arena words, their
+// One thread's share of a gather pass: up to NP arena words, their
 // expected epochs and LDS destinations, and which of them are still pending.
+template <int NP>
 struct GatherSlots {
   unsigned pending;
   unsigned pk;                      // slots holding pair words
-  unsigned off[kGatherPer];
-  unsigned want[kGatherPer];
-  lds_float* dst[kGatherPer];       // 32-bit LDS addresses
+  unsigned off[NP];
+  unsigned want[NP];
+  lds_float* dst[NP];               // 32-bit LDS addresses
 };
 
-template <int NR>
-__device__ __forceinline__ GatherSlots gather_slots(const LLRange (&rg)[NR], int total, int seg) {
-  GatherSlots S;
+template <int NP, int NR>
+__device__ __forceinline__ GatherSlots<NP> gather_slots(const LLRange (&rg)[NR], int total, int seg) {
+  GatherSlots<NP> S;
   S.pending = 0;
   S.pk = 0;
 #pragma unroll
-  for (int k = 0; k < kGatherPer; ++k) {
+  for (int k = 0; k < NP; ++k) {
     int i = seg + (int)threadIdx.x + k * kThreads;
     S.off[k] = kOffNone;
     S.want[k] = 0u;
@@ -600,14 +601,16 @@ __device__ __forceinline__ GatherSlots gather_slots(const LLRange (&rg)[NR], int
   return S;
 }
 
-__device__ __forceinline__ void gather_issue(Rsrc arena, const GatherSlots& S, u32x2 (&v)[kGatherPer]) {
+template <int NP>
+__device__ __forceinline__ void gather_issue(Rsrc arena, const GatherSlots<NP>& S, u32x2 (&v)[NP]) {
 #pragma unroll
-  for (int k = 0; k < kGatherPer; ++k) v[k] = ld_ll(arena, ((S.pending >> k) & 1u) ? S.off[k] : kOffNone);
+  for (int k = 0; k < NP; ++k) v[k] = ld_ll(arena, ((S.pending >> k) & 1u) ? S.off[k] : kOffNone);
 }
 
-__device__ __forceinline__ void gather_take(GatherSlots& S, const u32x2 (&v)[kGatherPer]) {
+template <int NP>
+__device__ __forceinline__ void gather_take(GatherSlots<NP>& S, const u32x2 (&v)[NP]) {
 #pragma unroll
-  for (int k = 0; k < kGatherPer; ++k) {
+  for (int k = 0; k < NP; ++k) {
     const bool pk = (S.pk >> k) & 1u;
     if (((S.pending >> k) & 1u) && (pk ? v[k].y >> 16 : v[k].y) == S.want[k]) {
       if (pk) {
@@ -645,13 +648,14 @@ __device__ __forceinline__ bool poll_check(const Ctl& c, int& spins, long long& 
 // One poll round per return: a second round in flight, or a longer pause
 // between rounds, both measured slower (more poll traffic delays the data's
 // own propagation; a pause delays its detection).
-__device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherSlots& S, const Ctl& c) {
+template <int NP>
+__device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherSlots<NP>& S, const Ctl& c) {
   long long t0 = 0;
   int spins = 0;
   while (S.pending) {
     if (!poll_check(c, spins, t0)) return false;
     __builtin_amdgcn_s_sleep(1);
-    u32x2 v[kGatherPer];
+    u32x2 v[NP];
     gather_issue(arena, S, v);
     gather_take(S, v);
   }
@@ -676,23 +680,23 @@ __device__ __forceinline__ bool gather_wait(const Params& p, Rsrc arena, GatherS
 // measured slower: the exchange got no faster (the polls still meet the
 // streaming traffic beyond the compute unit) and the polling waves started
 // their share of the rows late.
-template <int NR, class Issue>
+template <int NP = kGatherPer, int NR, class Issue>
 __device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[NR], const Ctl& c,
                                           Issue&& issue) {
   const Rsrc arena = arena_rsrc(p);
   int total = 0;
 #pragma unroll
   for (int r = 0; r < NR; ++r) total += rg[r].n;
-  GatherSlots S = gather_slots(rg, total, 0);
+  GatherSlots<NP> S = gather_slots<NP>(rg, total, 0);
   {
-    u32x2 v[kGatherPer];
+    u32x2 v[NP];
     gather_issue(arena, S, v);
     issue();
     gather_take(S, v);
   }
   bool ok = gather_wait(p, arena, S, c);
-  for (int seg = kGatherPer * kThreads; seg < total && ok; seg += kGatherPer * kThreads) {
-    S = gather_slots(rg, total, seg);
+  for (int seg = NP * kThreads; seg < total && ok; seg += NP * kThreads) {
+    S = gather_slots<NP>(rg, total, seg);
     ok = gather_wait(p, arena, S, c);
   }
   return wg_all(ok, c.flag);
@@ -705,10 +709,10 @@ __device__ __forceinline__ bool ll_gather(const Params& p, const LLRange (&rg)[N
 
 // A gather that prefetches the next stage's weights (issue) and the small
 // loads needed right after it (early: the norm gains) behind its first poll.
-template <int NR, class Early, class Issue>
+template <int NP = kGatherPer, int NR, class Early, class Issue>
 __device__ __forceinline__ bool ll_gather_pf(const Params& p, const LLRange (&rg)[NR], const Ctl& c,
                                              Early&& early, Issue&& issue) {
-  return ll_gather(p, rg, c, [&]() {
+  return ll_gather<NP>(p, rg, c, [&]() {
     issue();
     early();
   });
@@ -2040,9 +2044,12 @@ __device__ __forceinline__ bool stage_moe_down(const Params& p, int step, int l,
   const LLRange rg[3] = {{p.off_u, A * p.Fe / 2, s.h, ll_flag(p, step, l, kSlotU), 1},
                          {p.off_x + g.r0, nown, s.xown, ll_flag(p, step, l, kSlotXO)},
                          {p.off_router, have_routing ? 0 : p.E, s.sums, ll_flag(p, step, l, kSlotRouter)}};
+  // 12 words per thread: the active experts' u (5,632 pair words for 8
+  // experts of 1,408) arrives in one pass instead of two, each pass costing a
+  // poll round trip; the extra slot registers only count in the MoE kernel
   const bool ok = have_routing
-                      ? ll_gather_pf(p, rg, c, [] {}, [&]() { pre = gemv_prefetch(g, moe_down_addr(p, l, s)); })
-                      : ll_gather(p, rg, c);
+                      ? ll_gather_pf<12>(p, rg, c, [] {}, [&]() { pre = gemv_prefetch(g, moe_down_addr(p, l, s)); })
+                      : ll_gather<12>(p, rg, c, [] {});
   if (!ok) return false;
   mark(tr);
   if (!have_routing) {
@@ -2336,7 +2343,11 @@ __device__ __forceinline__ const Params& fresh(const Params* pp) {
   return *(const Params*)c;
 }
 
-template <int G>
+// The persistent kernel, one build per query-head group G and FFN kind: a
+// dense build carries no expert code and the MoE build no dense FFN, so
+// each is allocated the registers of its own path (the dense G = 1 build
+// uses 212 VGPRs, the MoE one 240).
+template <int G, bool kMoe>
 __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restrict__ pp) {
   // 16-byte aligned: the GEMV reads the input vector with 16-byte LDS loads
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -2349,14 +2360,13 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
   Ctl c;
   Tracer tr{nullptr, 0};
   int tok, n_steps, L, pos0, trace_step;
-  bool moe, decode;
+  bool decode;
   unsigned long long* trace;
   {
     const Params& p = fresh(pp);
     s = lds_carve(p, smem);
     gs = make_sync(p.bar, p.err, (unsigned)p.n_wg, p.timeout_ticks, p.spin_limit);
     c = make_ctl(p, &flag);
-    moe = p.E != 0;
     decode = p.mode == kDecode;
     n_steps = p.n_steps;
     L = p.L;
@@ -2395,7 +2405,7 @@ __global__ __launch_bounds__(kThreads, 1) void mono_kernel(const Params* __restr
         if (!stage_oproj(p, step, l, p.tok_emb + (size_t)tok * p.d, wg, s, c, tr)) return;
       }
       mark(tr);
-      if (!moe) {
+      if constexpr (!kMoe) {
         if (!stage_gateup(fresh(pp), step, l, wg, s, c, tr)) return;
         mark(tr);
         if (!stage_down(fresh(pp), step, l, wg, s, c, tr)) return;
@@ -2576,17 +2586,20 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-static const void* mono_for(int group) {
+static const void* mono_for(int group, bool moe) {
   switch (group) {
-    case 1: return reinterpret_cast<const void*>(mono_kernel<1>);
-    case 2: return reinterpret_cast<const void*>(mono_kernel<2>);
-    default: return reinterpret_cast<const void*>(mono_kernel<4>);
+    case 1: return moe ? reinterpret_cast<const void*>(mono_kernel<1, true>)
+                       : reinterpret_cast<const void*>(mono_kernel<1, false>);
+    case 2: return moe ? reinterpret_cast<const void*>(mono_kernel<2, true>)
+                       : reinterpret_cast<const void*>(mono_kernel<2, false>);
+    default: return moe ? reinterpret_cast<const void*>(mono_kernel<4, true>)
+                        : reinterpret_cast<const void*>(mono_kernel<4, false>);
   }
 }
 
-int max_blocks_per_cu(int group, size_t lds_bytes) {
+int max_blocks_per_cu(int group, bool moe, size_t lds_bytes) {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mono_for(group), kThreads, lds_bytes) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mono_for(group, moe), kThreads, lds_bytes) !=
       hipSuccess)
     return 0;
   return nb;
@@ -2596,9 +2609,9 @@ hipError_t launch_mono(const Params& p, const Params* p_dev, size_t lds_bytes, b
                        hipStream_t s) {
   void* args[] = {const_cast<Params**>(&p_dev)};
   if (plain)
-    return hipLaunchKernel(mono_for(p.H / p.nkv), dim3(p.n_wg), dim3(kThreads), args,
+    return hipLaunchKernel(mono_for(p.H / p.nkv, p.E != 0), dim3(p.n_wg), dim3(kThreads), args,
                            (unsigned)lds_bytes, s);
-  return hipLaunchCooperativeKernel(mono_for(p.H / p.nkv), dim3(p.n_wg), dim3(kThreads), args,
+  return hipLaunchCooperativeKernel(mono_for(p.H / p.nkv, p.E != 0), dim3(p.n_wg), dim3(kThreads), args,
                                     (unsigned)lds_bytes, s);
 }
 

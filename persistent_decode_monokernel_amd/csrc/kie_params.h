@@ -89,7 +89,7 @@ struct Params {
 };
 
 // Host-visible launchers implemented next to the kernels.
-int max_blocks_per_cu(int group, size_t lds_bytes);
+int max_blocks_per_cu(int group, bool moe, size_t lds_bytes);
 // p_dev: a device copy of p (the persistent kernel re-reads it per stage)
 hipError_t launch_mono(const Params& p, const Params* p_dev, size_t lds_bytes, bool plain,
                        hipStream_t s);

@@ -344,7 +344,7 @@ int kie_create(const kie_config* cfg, const kie_weights* w, void* hip_stream, ki
   h->lds = (size_t)L.total * sizeof(float);
   if (h->lds > kMaxLdsBytes)
     return bail(fail(KIE_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has"));
-  const int per_cu = kie::max_blocks_per_cu(c.n_heads / c.n_kv_heads, h->lds);
+  const int per_cu = kie::max_blocks_per_cu(c.n_heads / c.n_kv_heads, c.n_experts != 0, h->lds);
   if (per_cu < 1 || (long long)per_cu * n_cu < p.n_wg)
     return bail(fail(KIE_ERR_OCCUPANCY, "grid of " + std::to_string(p.n_wg) +
                                             " workgroups cannot be co-resident (" +
