@@ -356,6 +356,14 @@ VARIANTS = {
     # GQA with two query heads per KV head and a head size of 64
     "gqa2_narrow": dict(name="tiny", n_heads=8, n_kv_heads=4, head_dim=32, prompt_len=80,
                         n_decode=40),
+    # the MoE build with grouped query heads: 2 and 4 query heads per KV head
+    # (the matrix-core attention), head size 32
+    "moe_gqa2_narrow": dict(name="moe", n_layers=2, d_model=256, n_heads=8, n_kv_heads=4,
+                            head_dim=32, vocab_in=4096, vocab_out=4096, n_experts=8, top_k=2,
+                            n_shared_experts=1, expert_hidden=128, prompt_len=64, n_decode=32),
+    "moe_gqa4_narrow": dict(name="moe", n_layers=2, d_model=256, n_heads=8, n_kv_heads=2,
+                            head_dim=32, vocab_in=4096, vocab_out=4096, n_experts=8, top_k=2,
+                            n_shared_experts=1, expert_hidden=128, prompt_len=64, n_decode=32),
 }
 
 
